@@ -1,0 +1,184 @@
+"""Oracle for the grouped tril mask softmax: TEST INFRASTRUCTURE ONLY.
+
+Python access to the plain fp64 C oracle in ``gtms_oracle.c``. Only ``tests/``, the smoke
+check in ``__graft_entry__`` and the CPU-baseline leg of ``bench.py`` may import this
+package. The GPU product package never imports it, and it imports nothing of the product.
+
+Arrays cross this module as numpy arrays holding the raw element bits: ``float32`` for
+binary32, ``uint16`` for binary16 and bfloat16 (``dtype`` code 0, 1, 2, the same codes the
+C oracle uses).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "gtms_oracle.c")
+LIB = os.path.join(HERE, "liboracle_gtms.so")
+
+F32, F16, BF16 = 0, 1, 2
+STORAGE = {F32: np.float32, F16: np.uint16, BF16: np.uint16}
+
+GCC_FLAGS = ["-O2", "-std=gnu99", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math"]
+
+
+def build(src: str = SRC, out: str = LIB) -> str:
+    """Compile the oracle with gcc (IEEE arithmetic: no fast-math, no FMA contraction)."""
+    subprocess.run(["gcc", *GCC_FLAGS, f"-I{HERE}", src, "-o", out + ".tmp", "-lm"],
+                   check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def _ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _check(x: np.ndarray, dtype: int) -> np.ndarray:
+    if dtype not in STORAGE:
+        raise ValueError(f"unknown element type code {dtype}")
+    if x.dtype != STORAGE[dtype]:
+        raise TypeError(f"dtype code {dtype} expects storage {STORAGE[dtype]}, got {x.dtype}")
+    return np.ascontiguousarray(x)
+
+
+def _lens(seq_lens, n: int) -> np.ndarray:
+    sl = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    if sl.shape != (n,):
+        raise ValueError(f"expected {n} lengths, got shape {sl.shape}")
+    return sl
+
+
+class Oracle:
+    """One loaded copy of the C oracle (the default one, or a test build of it)."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        p, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+        for name in ("gtms_oracle_f64", "gtms_oracle"):
+            fn = getattr(lib, name)
+            fn.argtypes = [p, p, p, i64, i64, i64, f32, i32]
+            fn.restype = i32
+        lib.gtms_oracle_rows_f64.argtypes = [p, p, p, p, i64, i64, f32, i32]
+        lib.gtms_oracle_rows_f64.restype = i32
+        lib.gtms_oracle_backward_f64.argtypes = [p, p, p, p, i64, i64, i64, f32, i32]
+        lib.gtms_oracle_backward_f64.restype = i32
+        lib.gtms_oracle_decode.argtypes = [ctypes.c_uint32, i32]
+        lib.gtms_oracle_decode.restype = ctypes.c_double
+        lib.gtms_oracle_encode.argtypes = [ctypes.c_double, i32]
+        lib.gtms_oracle_encode.restype = ctypes.c_uint32
+        self.lib = lib
+        self.path = path
+
+    @staticmethod
+    def _status(st: int, what: str):
+        if st != 0:
+            raise RuntimeError(f"{what}: oracle status {st}")
+
+    def softmax_f64(self, x: np.ndarray, seq_lens, scale: float = 1.0,
+                    dtype: int = F32) -> np.ndarray:
+        """fp64 results for x of shape [B, M, S, S] (raw element storage)."""
+        x = _check(x, dtype)
+        B, M, S, S2 = x.shape
+        assert S == S2
+        sl = _lens(seq_lens, B)
+        y = np.empty(x.shape, dtype=np.float64)
+        self._status(self.lib.gtms_oracle_f64(_ptr(x), _ptr(y), _ptr(sl), B, M, S, scale,
+                                              dtype), "gtms_oracle_f64")
+        return y
+
+    def softmax(self, x: np.ndarray, seq_lens, scale: float = 1.0,
+                dtype: int = F32) -> np.ndarray:
+        """Results rounded to nearest-even into the element type (same storage as x)."""
+        x = _check(x, dtype)
+        B, M, S, S2 = x.shape
+        assert S == S2
+        sl = _lens(seq_lens, B)
+        y = np.empty_like(x)
+        self._status(self.lib.gtms_oracle(_ptr(x), _ptr(y), _ptr(sl), B, M, S, scale, dtype),
+                     "gtms_oracle")
+        return y
+
+    def softmax_rows_f64(self, rows: np.ndarray, row_index, seq_len, scale: float = 1.0,
+                         dtype: int = F32) -> np.ndarray:
+        """fp64 results for independent rows: rows[i] (length S) is row row_index[i] of a
+        plane whose batch has raw valid length seq_len[i]."""
+        rows = _check(rows, dtype)
+        n, S = rows.shape
+        ri = np.ascontiguousarray(np.asarray(row_index, dtype=np.int64))
+        sl = _lens(seq_len, n)
+        assert ri.shape == (n,)
+        y = np.empty((n, S), dtype=np.float64)
+        self._status(self.lib.gtms_oracle_rows_f64(_ptr(rows), _ptr(y), _ptr(ri), _ptr(sl),
+                                                   n, S, scale, dtype),
+                     "gtms_oracle_rows_f64")
+        return y
+
+    def backward_f64(self, y: np.ndarray, dy: np.ndarray, seq_lens, scale: float = 1.0,
+                     dtype: int = F32) -> np.ndarray:
+        """fp64 gradient with respect to the input, given the output y and upstream dy."""
+        y = _check(y, dtype)
+        dy = _check(dy, dtype)
+        B, M, S, S2 = y.shape
+        assert S == S2 and dy.shape == y.shape
+        sl = _lens(seq_lens, B)
+        dx = np.empty(y.shape, dtype=np.float64)
+        self._status(self.lib.gtms_oracle_backward_f64(_ptr(y), _ptr(dy), _ptr(dx), _ptr(sl),
+                                                       B, M, S, scale, dtype),
+                     "gtms_oracle_backward_f64")
+        return dx
+
+    def decode(self, bits: int, dtype: int) -> float:
+        return self.lib.gtms_oracle_decode(int(bits), dtype)
+
+    def encode(self, v: float, dtype: int) -> int:
+        return int(self.lib.gtms_oracle_encode(float(v), dtype))
+
+    def decode_array(self, x: np.ndarray, dtype: int) -> np.ndarray:
+        """Exact fp64 values of raw element storage, through the oracle's own codec."""
+        x = _check(x, dtype)
+        flat = x.view(np.uint32) if dtype == F32 else x
+        out = np.array([self.lib.gtms_oracle_decode(int(b), dtype) for b in flat.reshape(-1)],
+                       dtype=np.float64)
+        return out.reshape(x.shape)
+
+
+_default: Oracle | None = None
+
+
+def default() -> Oracle:
+    """The oracle built from ``gtms_oracle.c`` (rebuilt when the source is newer)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            build()
+        _default = Oracle(LIB)
+    return _default
+
+
+def softmax_f64(*a, **k):
+    return default().softmax_f64(*a, **k)
+
+
+def softmax(*a, **k):
+    return default().softmax(*a, **k)
+
+
+def softmax_rows_f64(*a, **k):
+    return default().softmax_rows_f64(*a, **k)
+
+
+def backward_f64(*a, **k):
+    return default().backward_f64(*a, **k)
+
+
+def decode(bits: int, dtype: int) -> float:
+    return default().decode(bits, dtype)
+
+
+def encode(v: float, dtype: int) -> int:
+    return default().encode(v, dtype)

@@ -1,0 +1,299 @@
+/*
+ * Oracle for the grouped tril mask softmax: TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously correct CPU implementation in fp64 of what the GPU path
+ * computes. Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+ * load it. It shares no code, header, table or helper with the GPU library, and neither
+ * side includes or links the other. Single-threaded on purpose.
+ *
+ * What it computes comes from the page "Fused grouped tril mask softmax"
+ * (github aoxy/Attention-Mask-Optimization, README):
+ *   - the operator-behaviour section (a torch loop giving the fused computation): X has
+ *     shape [B, M, S, S]; every plane of batch b shares one valid length L_b; element
+ *     (row, col) is kept when row < L_b, col < L_b and row >= col; kept elements go
+ *     through a softmax along the row; the rest are filled with the most negative finite
+ *     value before that softmax, so they contribute nothing;
+ *   - the three masks printed after that listing (S = 5, lengths 3, 4, 5), which show the
+ *     kept set row by row;
+ *   - the printed output, whose rows at or beyond L_b and whose upper triangle are zero.
+ * The listing finally sets every element equal to 1/S to zero. That step exists only to
+ * erase the uniform rows its softmax produces for fully masked rows; here a row with no
+ * kept element is written as zeros directly, and a kept element is never zeroed because of
+ * its value.
+ *
+ * The scale factor multiplies the scores before the softmax, as in the page
+ * "优化ScaledMaskSoftmax算子" (ScaledMaskSoftmax article), sections 2.1 and 4.1.
+ *
+ * Readings where the pages are silent (each is listed with its reason in the design notes):
+ *   - seq_lens values are clamped to [0, S] (the listing's predicate tolerates any value);
+ *   - results are rounded to nearest, ties to even, into the element type;
+ *   - a zero is +0.0;
+ *   - NaN or infinity inside a kept prefix propagates by IEEE arithmetic.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "gtms_oracle.h"
+
+enum { OK = 0, ERR_ARG = 1, ERR_DTYPE = 2 };
+
+/* ------------------------------------------------------------------------------------
+ * Element codec. A binary floating-point format with `ebits` exponent bits and `pbits`
+ * stored fraction bits, exponent bias 2^(ebits-1) - 1 (IEEE 754 layout):
+ *   binary32: 8 / 23, binary16: 5 / 10, bfloat16: 8 / 7.
+ * ------------------------------------------------------------------------------------ */
+static int format_of(int dtype, int* ebits, int* pbits, int* bytes) {
+    switch (dtype) {
+        case 0: *ebits = 8; *pbits = 23; *bytes = 4; return 1;
+        case 1: *ebits = 5; *pbits = 10; *bytes = 2; return 1;
+        case 2: *ebits = 8; *pbits = 7; *bytes = 2; return 1;
+        default: return 0;
+    }
+}
+
+static double decode_bits(uint32_t bits, int ebits, int pbits) {
+    uint32_t emax = (1u << ebits) - 1;
+    int bias = (int)(emax >> 1);
+    uint32_t sign = (bits >> (ebits + pbits)) & 1u;
+    uint32_t e = (bits >> pbits) & emax;
+    uint32_t f = bits & ((1u << pbits) - 1);
+    double mag;
+    if (e == emax)
+        mag = f ? NAN : INFINITY;
+    else if (e == 0)
+        mag = ldexp((double)f, 1 - bias - pbits); /* subnormal: f * 2^(emin - pbits) */
+    else
+        mag = ldexp((double)(f | (1u << pbits)), (int)e - bias - pbits);
+    return sign ? -mag : mag;
+}
+
+/* Round v to the nearest representable value, ties to even, and return its bits. */
+static uint32_t encode_bits(double v, int ebits, int pbits) {
+    uint32_t emax = (1u << ebits) - 1;
+    int bias = (int)(emax >> 1);
+    int emin = 1 - bias;
+    uint32_t sign = signbit(v) ? (1u << (ebits + pbits)) : 0u;
+    if (isnan(v)) return sign | (emax << pbits) | (1u << (pbits - 1));
+    double a = fabs(v);
+    if (isinf(a)) return sign | (emax << pbits);
+    if (a == 0.0) return sign;
+    int E;
+    frexp(a, &E);
+    E -= 1; /* now 2^E <= a < 2^(E+1) */
+    if (E < emin) E = emin; /* below the normal range the spacing stays 2^(emin - pbits) */
+    /* a / spacing, where spacing = 2^(E - pbits); scaling by a power of two is exact, and
+     * nearbyint rounds to the nearest integer, ties to even (default rounding mode). */
+    double q = nearbyint(ldexp(a, pbits - E));
+    if (q >= ldexp(1.0, pbits + 1)) { /* rounded up into the next binade */
+        q = ldexp(q, -1);
+        E += 1;
+    }
+    if (E > bias) return sign | (emax << pbits); /* beyond the largest finite value */
+    uint32_t n = (uint32_t)q;
+    if (n < (1u << pbits)) return sign | n; /* subnormal, E == emin */
+    return sign | ((uint32_t)(E + bias) << pbits) | (n - (1u << pbits));
+}
+
+static double load_elem(const void* base, int64_t i, int dtype) {
+    int ebits, pbits, bytes;
+    format_of(dtype, &ebits, &pbits, &bytes);
+    uint32_t bits;
+    if (bytes == 4) {
+        memcpy(&bits, (const unsigned char*)base + 4 * i, 4);
+    } else {
+        uint16_t h;
+        memcpy(&h, (const unsigned char*)base + 2 * i, 2);
+        bits = h;
+    }
+    return decode_bits(bits, ebits, pbits);
+}
+
+static void store_elem(void* base, int64_t i, double v, int dtype) {
+    int ebits, pbits, bytes;
+    format_of(dtype, &ebits, &pbits, &bytes);
+    uint32_t bits = encode_bits(v, ebits, pbits);
+    if (bytes == 4) {
+        memcpy((unsigned char*)base + 4 * i, &bits, 4);
+    } else {
+        uint16_t h = (uint16_t)bits;
+        memcpy((unsigned char*)base + 2 * i, &h, 2);
+    }
+}
+
+double gtms_oracle_decode(uint32_t bits, int dtype) {
+    int ebits, pbits, bytes;
+    if (!format_of(dtype, &ebits, &pbits, &bytes)) return NAN;
+    return decode_bits(bits, ebits, pbits);
+}
+
+uint32_t gtms_oracle_encode(double v, int dtype) {
+    int ebits, pbits, bytes;
+    if (!format_of(dtype, &ebits, &pbits, &bytes)) return 0;
+    return encode_bits(v, ebits, pbits);
+}
+
+/* ------------------------------------------------------------------------------------
+ * The operation.
+ * ------------------------------------------------------------------------------------ */
+
+/* Valid length of a batch: the raw value clamped to [0, S]. */
+static int64_t valid_length(int32_t raw, int64_t S) {
+    int64_t L = raw;
+    if (L < 0) L = 0;
+    if (L > S) L = S;
+    return L;
+}
+
+/* The mask predicate of the operator-behaviour listing: an element is kept when neither
+ * its row nor its column reaches the valid length and it lies on or below the diagonal. */
+static int kept(int64_t row, int64_t col, int64_t L) {
+    int invalid = row >= L || col >= L;
+    return !invalid && row >= col;
+}
+
+/* One row of S elements at x (element type dtype), row index r, valid length L.
+ * Writes S fp64 results to y. */
+static void softmax_row(const void* x, int64_t r, int64_t L, int64_t S, double scale,
+                        int dtype, double* y) {
+    /* z_c = scale * x_c for the kept columns; mu = their maximum. */
+    double mu = -INFINITY;
+    int64_t nkept = 0;
+    for (int64_t c = 0; c < S; ++c) {
+        if (!kept(r, c, L)) continue;
+        double z = scale * load_elem(x, c, dtype);
+        if (z > mu) mu = z;
+        ++nkept;
+    }
+    if (nkept == 0) { /* a padded row: every element is masked */
+        for (int64_t c = 0; c < S; ++c) y[c] = 0.0;
+        return;
+    }
+    /* denominator: sum over kept columns of exp(z_c - mu), in column order */
+    double den = 0.0;
+    for (int64_t c = 0; c < S; ++c) {
+        if (!kept(r, c, L)) continue;
+        den += exp(scale * load_elem(x, c, dtype) - mu);
+    }
+    for (int64_t c = 0; c < S; ++c) {
+        if (kept(r, c, L))
+            y[c] = exp(scale * load_elem(x, c, dtype) - mu) / den;
+        else
+            y[c] = 0.0;
+    }
+}
+
+/* Checks shared by the entry points; on success *n_elem = B*M*S*S. */
+static int check_shape(const void* a, const void* b, const int32_t* seq_lens, int64_t B,
+                       int64_t M, int64_t S, int dtype, int64_t* n_elem) {
+    int ebits, pbits, bytes;
+    if (!format_of(dtype, &ebits, &pbits, &bytes)) return ERR_DTYPE;
+    if (B < 0 || M < 0 || S < 0) return ERR_ARG;
+    int64_t n = 1;
+    if (__builtin_mul_overflow(n, B, &n) || __builtin_mul_overflow(n, M, &n) ||
+        __builtin_mul_overflow(n, S, &n) || __builtin_mul_overflow(n, S, &n))
+        return ERR_ARG;
+    if (n > 0 && (!a || !b || !seq_lens)) return ERR_ARG;
+    *n_elem = n;
+    return OK;
+}
+
+int gtms_oracle_f64(const void* in, double* out, const int32_t* seq_lens, int64_t B,
+                    int64_t M, int64_t S, float scale, int dtype) {
+    int64_t n;
+    int st = check_shape(in, out, seq_lens, B, M, S, dtype, &n);
+    if (st != OK || n == 0) return st;
+    int ebits, pbits, bytes;
+    format_of(dtype, &ebits, &pbits, &bytes);
+    for (int64_t b = 0; b < B; ++b) {
+        int64_t L = valid_length(seq_lens[b], S);
+        for (int64_t m = 0; m < M; ++m) {
+            for (int64_t r = 0; r < S; ++r) {
+                int64_t off = ((b * M + m) * S + r) * S;
+                softmax_row((const unsigned char*)in + off * bytes, r, L, S, (double)scale,
+                            dtype, out + off);
+            }
+        }
+    }
+    return OK;
+}
+
+int gtms_oracle(const void* in, void* out, const int32_t* seq_lens, int64_t B, int64_t M,
+                int64_t S, float scale, int dtype) {
+    int64_t n;
+    int st = check_shape(in, out, seq_lens, B, M, S, dtype, &n);
+    if (st != OK || n == 0) return st;
+    int ebits, pbits, bytes;
+    format_of(dtype, &ebits, &pbits, &bytes);
+    double* y = (double*)malloc((size_t)S * sizeof(double));
+    if (!y) return ERR_ARG;
+    for (int64_t b = 0; b < B; ++b) {
+        int64_t L = valid_length(seq_lens[b], S);
+        for (int64_t m = 0; m < M; ++m) {
+            for (int64_t r = 0; r < S; ++r) {
+                int64_t off = ((b * M + m) * S + r) * S;
+                softmax_row((const unsigned char*)in + off * bytes, r, L, S, (double)scale,
+                            dtype, y);
+                for (int64_t c = 0; c < S; ++c) store_elem(out, off + c, y[c], dtype);
+            }
+        }
+    }
+    free(y);
+    return OK;
+}
+
+int gtms_oracle_rows_f64(const void* rows_in, double* rows_out, const int64_t* row,
+                         const int32_t* seq_len, int64_t nrows, int64_t S, float scale,
+                         int dtype) {
+    int ebits, pbits, bytes;
+    if (!format_of(dtype, &ebits, &pbits, &bytes)) return ERR_DTYPE;
+    if (nrows < 0 || S < 0) return ERR_ARG;
+    if (nrows == 0 || S == 0) return OK;
+    if (!rows_in || !rows_out || !row || !seq_len) return ERR_ARG;
+    for (int64_t i = 0; i < nrows; ++i) {
+        if (row[i] < 0 || row[i] >= S) return ERR_ARG;
+    }
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t L = valid_length(seq_len[i], S);
+        softmax_row((const unsigned char*)rows_in + i * S * bytes, row[i], L, S,
+                    (double)scale, dtype, rows_out + i * S);
+    }
+    return OK;
+}
+
+/* Backward. For one kept row, y = softmax(z) with z = scale * x, and the softmax
+ * derivative dy_i/dz_j = y_i (delta_ij - y_j) (page "ops(8) self-attention CUDA (下)",
+ * section 2.1, softmax derivative) gives, for an upstream gradient g,
+ *   dx_j = scale * sum_i g_i y_i (delta_ij - y_j) = scale * y_j * (g_j - sum_i g_i y_i),
+ * the sums running over the kept columns of the row. Masked elements and padded rows do
+ * not reach the output, so their gradient is zero. */
+int gtms_oracle_backward_f64(const void* y, const void* dy, double* dx,
+                             const int32_t* seq_lens, int64_t B, int64_t M, int64_t S,
+                             float scale, int dtype) {
+    int64_t n;
+    int st = check_shape(y, dx, seq_lens, B, M, S, dtype, &n);
+    if (st != OK || n == 0) return st;
+    if (!dy) return ERR_ARG;
+    for (int64_t b = 0; b < B; ++b) {
+        int64_t L = valid_length(seq_lens[b], S);
+        for (int64_t m = 0; m < M; ++m) {
+            for (int64_t r = 0; r < S; ++r) {
+                int64_t off = ((b * M + m) * S + r) * S;
+                double dot = 0.0;
+                for (int64_t c = 0; c < S; ++c) {
+                    if (kept(r, c, L))
+                        dot += load_elem(dy, off + c, dtype) * load_elem(y, off + c, dtype);
+                }
+                for (int64_t c = 0; c < S; ++c) {
+                    if (kept(r, c, L))
+                        dx[off + c] = (double)scale * load_elem(y, off + c, dtype) *
+                                      (load_elem(dy, off + c, dtype) - dot);
+                    else
+                        dx[off + c] = 0.0;
+                }
+            }
+        }
+    }
+    return OK;
+}

@@ -1,0 +1,50 @@
+/*
+ * Oracle for the grouped tril mask softmax: TEST INFRASTRUCTURE ONLY.
+ *
+ * Declarations of the plain fp64 CPU oracle in gtms_oracle.c. Only the test suite, the
+ * smoke check and the benchmark's CPU-baseline leg may load this library. The GPU product
+ * library neither includes this header nor links the oracle, and the oracle includes
+ * nothing of the product.
+ *
+ * Element-type codes: 0 = IEEE binary32, 1 = IEEE binary16, 2 = bfloat16.
+ * Status codes: 0 = ok, 1 = invalid argument, 2 = unknown element type.
+ */
+#ifndef GTMS_ORACLE_H
+#define GTMS_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Full tensor: in and out are host arrays of B*M*S*S elements, row-major [B, M, S, S];
+ * seq_lens holds B raw lengths (clamped to [0, S]). out receives fp64 results. */
+int gtms_oracle_f64(const void* in, double* out, const int32_t* seq_lens, int64_t B,
+                    int64_t M, int64_t S, float scale, int dtype);
+
+/* Same, with every result rounded to nearest-even into the input's element type. */
+int gtms_oracle(const void* in, void* out, const int32_t* seq_lens, int64_t B, int64_t M,
+                int64_t S, float scale, int dtype);
+
+/* Independent rows: rows_in holds nrows rows of S elements; row i is row index row[i] of a
+ * plane whose batch has raw length seq_len[i]. rows_out receives nrows*S fp64 results. */
+int gtms_oracle_rows_f64(const void* rows_in, double* rows_out, const int64_t* row,
+                         const int32_t* seq_len, int64_t nrows, int64_t S, float scale,
+                         int dtype);
+
+/* Backward of the same operation: given the forward output Y and an upstream gradient dY
+ * (both [B, M, S, S] in the element type), write dX in fp64. */
+int gtms_oracle_backward_f64(const void* y, const void* dy, double* dx,
+                             const int32_t* seq_lens, int64_t B, int64_t M, int64_t S,
+                             float scale, int dtype);
+
+/* The element codec, exported so that it can be pinned on its own. */
+double gtms_oracle_decode(uint32_t bits, int dtype);
+uint32_t gtms_oracle_encode(double v, int dtype);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif
