@@ -1,0 +1,215 @@
+#!/usr/bin/env python3
+"""Benchmark of the grouped tril mask softmax on one MI355X.
+
+One step is one call of the whole operation (gtms_forward: decomposition, padded rows,
+prefix loads, max, exp/sum, normalise, zero tails) over one batch of synthetic scores that
+are already resident in HBM. The default workload is the README's timed shape
+X[3, 64, 1000, 1000] in binary32 with seeded lengths; the other workloads are parity-test
+shapes and can be measured with --workload.
+
+Prints ONE JSON line. value = effective HBM throughput over the algorithmic bytes of a
+step: the kept lower-triangle reads plus the full S*S writes,
+    bytes = esize * (sum_b M * L_b (L_b + 1) / 2 + B * M * S^2).
+The roofline object reports the same bytes over the kernel's average duration measured
+with HIP events on the launch stream, against the 8 TB/s HBM peak of the MI355X. The
+cpu_baseline object times the fp64 CPU oracle on the same workload on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "ms and effective HBM GB/s (% of peak) for [B,M,S,S] masked softmax"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "variable_length_causal_amd", "csrc", f)
+                  for f in ("device_common.h", "forward_kernels.h", "gtms_api.hip")]
+
+
+def algorithmic_bytes(w: workloads.Workload, lens) -> int:
+    S = w.S
+    reads = sum(w.M * min(max(int(L), 0), S) * (min(max(int(L), 0), S) + 1) // 2 for L in lens)
+    writes = w.B * w.M * S * S
+    return w.esize * (reads + writes)
+
+
+def kernel_sources_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, or
+    None if there is none for this workload or the kernel sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = data.get(workload)
+    if not ent or ent.get("kernel_sources_sha256") != kernel_sources_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(x_dev, lens, w: workloads.Workload, budget_s: float):
+    """Time the CPU oracle (single-threaded, as it stands) on whole planes of the same
+    input: all planes if they fit the time budget, else the first planes of every batch."""
+    import oracle
+    import torch
+    # estimate the per-plane cost from one plane of the largest length
+    probe_b = int(np.argmax(lens))
+    xs = workloads.to_storage(x_dev[probe_b:probe_b + 1, :1].cpu())
+    t0 = time.perf_counter()
+    oracle.softmax(xs, lens[probe_b:probe_b + 1], w.scale, w.dtype)
+    per_plane = max(time.perf_counter() - t0, 1e-6)
+    k = int(max(1, min(w.M, budget_s / (per_plane * w.B))))
+    sample = x_dev[:, :k].contiguous().cpu()
+    xs = workloads.to_storage(sample)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    oracle.softmax(xs, lens, w.scale, w.dtype)
+    dt = time.perf_counter() - t0
+    sub = workloads.Workload(w.name, w.B, k, w.S, w.dtype, w.sigma, w.scale)
+    nbytes = algorithmic_bytes(sub, lens)
+    what = "all planes" if k == w.M else f"planes m < {k} of every batch"
+    return {
+        "value": round(nbytes / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{what} ({w.B * k} of {w.B * w.M} planes, {nbytes / 1e6:.1f} MB "
+                  f"algorithmic) of the same seeded input, fp64 C oracle, one thread, "
+                  f"{dt:.2f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="readme_f32_3x64x1000",
+                    choices=sorted(k for k in workloads.WORKLOADS if "example" not in k))
+    ap.add_argument("--path", default="auto", choices=["auto", "wave", "block", "stream"])
+    ap.add_argument("--flags", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain device copy of known size (for HBM counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the operation shards by planes with no communication; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import variable_length_causal_amd as g
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workloads.WORKLOADS[args.workload]
+    lens = workloads.seq_lens(w)
+    sl = torch.as_tensor(lens).to(dev)
+    step_bytes = algorithmic_bytes(w, lens)
+    tensor_bytes = w.B * w.M * w.S * w.S * w.esize
+
+    # rotate over enough (input, output) pairs that consecutive uses of one pair are
+    # separated by far more than the 256 MB last-level cache; the inputs are resident
+    # before the timed region starts
+    nsets = int(min(4, max(1, (3 << 30) // tensor_bytes + 1)))
+    xs = [workloads.scores_device(w.shape, w.dtype, w.sigma, w.x_seed + i, dev) for i in range(nsets)]
+    ys = [torch.empty_like(xs[0]) for _ in range(nsets)]
+    torch.cuda.synchronize()
+
+    def step(i):
+        g.forward(xs[i % nsets], sl, w.scale, out=ys[i % nsets], path=args.path, flags=args.flags)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [a.elapsed_time(b) for a, b in ev]
+    avg_kernel_ms = float(np.mean(kernel_ms))
+    ms_per_step = wall * 1e3 / args.steps
+
+    if args.copy_calibration:  # plain copy of a known size, outside the timed region
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = step_bytes / (avg_kernel_ms * 1e-3) / 1e9
+    traffic = measured_traffic(args.workload)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": workloads.DTYPE_NAMES[w.dtype],
+        "data": "synthetic (seeded normal scores generated on the device, seeded lengths)",
+        "config": {
+            "workload": w.name,
+            "B": w.B, "M": w.M, "S": w.S,
+            "seq_lens": [int(v) for v in lens],
+            "scale": w.scale,
+            "path": args.path,
+            "bytes_per_step": step_bytes,
+            "kernel_ms_min": round(float(np.min(kernel_ms)), 5),
+            "kernel_ms_median": round(float(np.median(kernel_ms)), 5),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(xs[0], lens, w, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

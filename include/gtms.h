@@ -1,0 +1,108 @@
+/*
+ * gtms: grouped tril mask softmax on AMD Instinct MI355X (gfx950, CDNA4).
+ *
+ * The operation (page "Fused grouped tril mask softmax", github aoxy/Attention-Mask-
+ * Optimization README, operator-behaviour section and the masks printed after it):
+ * X holds attention scores of shape [B, M, S, S], row-major and contiguous. Every plane of
+ * batch b shares one valid length L_b = clamp(seq_lens[b], 0, S). For row r < L_b the
+ * output row is softmax(scale * X[b, m, r, 0..r]) in columns 0..r and +0.0 in columns
+ * r+1..S-1; every row r >= L_b is written as +0.0. The mask is computed from (r, c, L_b)
+ * and never loaded, and masked scores do not influence the result. The scale multiplies
+ * the scores before the softmax (page "优化ScaledMaskSoftmax算子", sections 2.1 and 4.1).
+ *
+ * Element types: binary32, binary16 and bfloat16 in memory; arithmetic in fp32 on the GPU
+ * (the mixed-precision scheme of the ScaledMaskSoftmax article, section 2.1). Results are
+ * rounded to nearest, ties to even, into the element type.
+ *
+ * Conventions of every entry point:
+ *   - all pointers are device pointers, owned by the caller; the library allocates no
+ *     memory and keeps no state between calls, so calls are re-entrant;
+ *   - work is queued on `stream` (a hipStream_t; NULL is the null stream) and the call
+ *     returns without waiting; the caller synchronises before reading results;
+ *   - B * M * S == 0 is a valid no-op;
+ *   - seq_lens values outside [0, S] are clamped on the device (they live in device
+ *     memory, so the host never inspects them);
+ *   - errors are returned as a gtms_status; nothing aborts and no exception crosses the
+ *     ABI. A failed call queues no work.
+ */
+#ifndef GTMS_H
+#define GTMS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type codes. */
+enum gtms_dtype { GTMS_F32 = 0, GTMS_F16 = 1, GTMS_BF16 = 2 };
+
+/* Status codes returned by every entry point. */
+enum gtms_status {
+    GTMS_OK = 0,
+    GTMS_ERR_INVALID_ARG = 1, /* negative size, null pointer, B*M*S*S overflows int64,
+                                 S above GTMS_MAX_S, or in/out partially overlapping */
+    GTMS_ERR_DTYPE = 2,       /* unknown element type code */
+    GTMS_ERR_ALIGN = 3,       /* a pointer not aligned to its element size */
+    GTMS_ERR_HIP = 4,         /* the HIP runtime refused the launch */
+    GTMS_ERR_PATH = 5         /* gtms_forward_ex: unknown path, or a path that cannot
+                                 serve this shape and alignment */
+};
+
+/* Largest supported row length. */
+#define GTMS_MAX_S (1 << 24)
+
+/*
+ * Forward: out = grouped tril mask softmax of in.
+ *   in, out   [B, M, S, S] elements of `dtype`, contiguous row-major. in == out (in place,
+ *             as the README's listing overwrites its scores) is allowed; any other overlap
+ *             is rejected with GTMS_ERR_INVALID_ARG.
+ *   seq_lens  B int32 valid lengths.
+ *   scale     multiplies the scores before the softmax; |scale * x * log2(e)| must stay
+ *             inside the fp32 range for the kept scores.
+ * Rows whose kept scores hold NaN or infinity produce NaN in their kept columns; their
+ * masked columns are still +0.0.
+ */
+int gtms_forward(const void* in, void* out, const int32_t* seq_lens, int64_t B, int64_t M,
+                 int64_t S, float scale, int dtype, void* stream);
+
+/* Kernel choice for gtms_forward_ex. AUTO is what gtms_forward uses. */
+enum gtms_path {
+    GTMS_PATH_AUTO = 0,
+    GTMS_PATH_WAVE = 1,   /* one 64-lane wavefront per row, the row's kept prefix held in
+                             registers (rows up to 4096 binary32 / 8192 16-bit elements) */
+    GTMS_PATH_BLOCK = 2,  /* one workgroup per row, per-wave (max, sum) partials merged
+                             through LDS (rows up to 32768 binary32 / 65536 16-bit) */
+    GTMS_PATH_STREAM = 3  /* one workgroup per row, two passes over the row: online
+                             (max, sum) then normalise (any row length) */
+};
+
+/* Option bits for gtms_forward_ex (0 = the defaults gtms_forward uses). */
+enum gtms_flags {
+    GTMS_FLAG_NO_PAIR = 1u << 0,     /* do not pair row r with row S-1-r in one work unit */
+    GTMS_FLAG_NO_XCD_ORDER = 1u << 1,/* plain block order instead of contiguous row ranges
+                                        per XCD */
+    GTMS_FLAG_CACHED_STORES = 1u << 2/* ordinary stores instead of non-temporal ones */
+};
+
+/*
+ * Forward with an explicit kernel choice and options. For one path every flag setting
+ * gives the same bits; different paths reduce in different orders, so they agree with each
+ * other only to within rounding. A path that cannot serve the shape (row too long for its
+ * registers) returns GTMS_ERR_PATH. Meant for tests and tuning.
+ */
+int gtms_forward_ex(const void* in, void* out, const int32_t* seq_lens, int64_t B,
+                    int64_t M, int64_t S, float scale, int dtype, int path, unsigned flags,
+                    void* stream);
+
+/* A static, human-readable description of a status code. */
+const char* gtms_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int gtms_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GTMS_H */

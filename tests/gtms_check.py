@@ -1,0 +1,53 @@
+"""Helpers of the GPU parity tests: the kept set, comparisons against the oracle."""
+from __future__ import annotations
+
+import numpy as np
+
+import workloads
+
+# spec tolerances: max |GPU - oracle fp64| on kept elements, per element type
+TOL = {workloads.F32: 2e-6, workloads.F16: 2e-3, workloads.BF16: 8e-3}
+
+
+def kept_mask(S: int, L: int) -> np.ndarray:
+    """bool [S, S]: element (r, c) is kept when c <= r < L (L clamped to [0, S])."""
+    L = min(max(int(L), 0), S)
+    r = np.arange(S)[:, None]
+    c = np.arange(S)[None, :]
+    return (c <= r) & (r < L)
+
+
+def to_f64(storage: np.ndarray, dtype: int) -> np.ndarray:
+    """Exact fp64 values of raw element storage (float32, or uint16 bits)."""
+    if dtype == workloads.F32:
+        return storage.astype(np.float64)
+    if dtype == workloads.F16:
+        return storage.view(np.float16).astype(np.float64)
+    return (storage.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def bits(storage: np.ndarray) -> np.ndarray:
+    return storage.view(np.uint32) if storage.dtype == np.float32 else storage.view(np.uint16)
+
+
+def check_against_oracle(out_storage: np.ndarray, ref64: np.ndarray, lens, dtype: int,
+                         tol: float | None = None) -> float:
+    """Masked elements must be +0 bit for bit; kept elements within the tolerance.
+    Returns the max abs error on kept elements."""
+    tol = TOL[dtype] if tol is None else tol
+    B, M, S, _ = out_storage.shape
+    got = to_f64(out_storage, dtype)
+    ob = bits(out_storage)
+    worst = 0.0
+    for b in range(B):
+        keep = kept_mask(S, lens[b])
+        for m in range(M):
+            masked_bits = ob[b, m][~keep]
+            assert not masked_bits.any(), f"nonzero bits in masked region b={b} m={m}"
+            if keep.any():
+                err = np.abs(got[b, m][keep] - ref64[b, m][keep])
+                e = float(np.nanmax(err)) if err.size else 0.0
+                assert np.all(np.isfinite(got[b, m][keep])), f"non-finite output b={b} m={m}"
+                assert e <= tol, f"b={b} m={m}: max error {e:.3g} > {tol:.3g}"
+                worst = max(worst, e)
+    return worst

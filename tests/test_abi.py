@@ -1,0 +1,77 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol, and rejects
+bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    inc = os.path.join(ROOT, "include")
+    for fn in sorted(os.listdir(inc)):
+        if fn.endswith(".h"):
+            text = open(os.path.join(inc, fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gtms_\w+)\s*\(", text, re.M)
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import variable_length_causal_amd as g
+    return g.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert "gtms_forward" in names and "gtms_status_string" in names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+
+
+def test_status_strings(lib):
+    import variable_length_causal_amd as g
+    for code in range(6):
+        assert g.status_string(code)
+    assert g.status_string(99) == "unknown status"
+    assert g.version() >= 100
+
+
+FAKE = 1 << 36  # a well-aligned pointer value that is never dereferenced
+
+
+def fwd(lib, x=FAKE, y=FAKE * 4, sl=FAKE * 8, B=1, M=1, S=8, scale=1.0, dtype=0):
+    return lib.gtms_forward(x, y, sl, B, M, S, scale, dtype, None)
+
+
+def test_argument_checks(lib):
+    assert fwd(lib, dtype=3) == 2                        # unknown element type
+    assert fwd(lib, dtype=-1) == 2
+    assert fwd(lib, B=-1) == 1                           # negative size
+    assert fwd(lib, S=-4) == 1
+    assert fwd(lib, x=0) == 1                            # null pointers
+    assert fwd(lib, y=0) == 1
+    assert fwd(lib, sl=0) == 1
+    assert fwd(lib, B=0, x=0, y=0, sl=0) == 0            # empty: valid no-op
+    assert fwd(lib, S=0, x=0, y=0, sl=0) == 0
+    assert fwd(lib, B=1 << 40, M=1 << 20, S=1 << 10) == 1  # B*M*S*S overflows
+    assert fwd(lib, S=(1 << 24) + 1) == 1                # beyond GTMS_MAX_S
+    assert fwd(lib, x=FAKE + 2, dtype=0) == 3            # misaligned binary32
+    assert fwd(lib, y=FAKE * 4 + 1, dtype=1) == 3        # misaligned binary16
+    assert fwd(lib, sl=FAKE * 8 + 2) == 3                # misaligned lengths
+    # partial overlap of in and out (identical pointers are allowed: in place)
+    assert fwd(lib, x=FAKE, y=FAKE + 64, S=8) == 1
+
+
+def test_path_checks(lib):
+    def ex(path, S=8, dtype=0, flags=0):
+        return lib.gtms_forward_ex(FAKE, FAKE * 4, FAKE * 8, 1, 1, S, 1.0, dtype, path, flags,
+                                   None)
+    assert ex(7) == 5 and ex(-1) == 5                    # unknown path
+    assert ex(1, S=4097, dtype=0) == 5                   # row too long for the wave path
+    assert ex(1, S=8193, dtype=1) == 5
+    assert ex(2, S=32769, dtype=0) == 5                  # ... and for the block path

@@ -1,0 +1,290 @@
+"""GPU parity: the HIP kernels, called through the C ABI, against the CPU oracle.
+
+Masked elements must be +0.0 bit for bit; kept elements must lie within the element type's
+tolerance of the oracle's fp64 result (binary32 2e-6, binary16 2e-3, bfloat16 8e-3).
+Small shapes are compared element by element; the full workload shapes, launched exactly
+as the benchmark launches them, are compared on sampled rows plus properties checked on
+every row (exact zeros, row sums).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gtms_check import TOL, bits, check_against_oracle, kept_mask, to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("GPU tests need a visible GPU", allow_module_level=True)
+
+import variable_length_causal_amd as g  # noqa: E402
+
+DTYPES = [workloads.F32, workloads.F16, workloads.BF16]
+DNAME = {workloads.F32: "f32", workloads.F16: "f16", workloads.BF16: "bf16"}
+# rows each path holds in registers (elements), as in include/gtms.h
+CAP = {("wave", 4): 4096, ("wave", 2): 8192, ("block", 4): 32768, ("block", 2): 65536}
+
+
+def esize(dtype):
+    return 4 if dtype == workloads.F32 else 2
+
+
+def path_ok(path, S, dtype):
+    return path in ("auto", "stream") or S <= CAP[(path, esize(dtype))]
+
+
+def run_gpu(x_cpu, lens, scale, path="auto", flags=0, out=None):
+    x = x_cpu.cuda()
+    sl = torch.as_tensor(np.asarray(lens, dtype=np.int32)).cuda()
+    y = g.forward(x, sl, scale, out=out, path=path, flags=flags)
+    torch.cuda.synchronize()
+    return y
+
+
+def check_small(x_cpu, lens, scale, dtype, path="auto", flags=0):
+    print(f"case shape={tuple(x_cpu.shape)} dtype={DNAME[dtype]} path={path} flags={flags} "
+          f"lens={list(lens)} scale={scale}", flush=True)
+    y = run_gpu(x_cpu, lens, scale, path, flags)
+    out = workloads.to_storage(y.cpu())
+    ref = oracle.softmax_f64(workloads.to_storage(x_cpu), lens, scale, dtype)
+    return check_against_oracle(out, ref, lens, dtype)
+
+
+# ------------------------------------------------------------------------ small shapes
+
+def test_worked_example_shape():
+    """The README's worked-example shape [3, 2, 5, 5] with lengths 3, 4, 5."""
+    w = workloads.WORKLOADS["example_f32_3x2x5"]
+    x = workloads.scores_cpu(w.shape, w.dtype, w.sigma, w.x_seed)
+    lens = workloads.seq_lens(w)
+    for path in ("auto", "wave", "block", "stream"):
+        check_small(x, lens, w.scale, w.dtype, path)
+
+
+S_SWEEP = [1, 2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 31, 33, 63, 64, 65, 127, 128, 129, 255, 256,
+           257, 511, 513, 1000, 1023, 1025]
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DNAME[d])
+def test_shape_sweep(dtype):
+    """Every path over row lengths that cover one vector, several vectors, several 64-lane
+    sweeps and ragged tails; lengths 0, 1, partial, S and beyond S, and negative."""
+    for S in S_SWEEP:
+        lens = [S, max(1, S // 2), 0, S + 3, -1, 1]
+        x = workloads.scores_cpu((len(lens), 2, S, S), dtype, 1.5, seed=3000 + S)
+        ref = oracle.softmax_f64(workloads.to_storage(x), lens, 0.7, dtype)
+        for path in ("auto", "wave", "block", "stream"):
+            print(f"sweep S={S} dtype={DNAME[dtype]} path={path}", flush=True)
+            y = run_gpu(x, lens, 0.7, path)
+            check_against_oracle(workloads.to_storage(y.cpu()), ref, lens, dtype)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DNAME[d])
+def test_unaligned_rows_take_the_scalar_path(dtype):
+    """A tensor that starts off a 16-byte boundary, and rows whose byte length is not a
+    multiple of 16, still give exact results (element-wide accesses)."""
+    tdt = workloads.torch_dtype(dtype)
+    for S in (12, 40, 100):
+        lens = [S, S // 3, 0]
+        x_cpu = workloads.scores_cpu((3, 2, S, S), dtype, 1.0, seed=4000 + S)
+        n = x_cpu.numel()
+        for path in ("auto", "wave", "block", "stream"):
+            buf_in = torch.zeros(n + 1, dtype=tdt, device="cuda")
+            buf_out = torch.zeros(n + 1, dtype=tdt, device="cuda")
+            x = buf_in[1:].view(x_cpu.shape)
+            x.copy_(x_cpu.cuda())
+            out = buf_out[1:].view(x_cpu.shape)
+            assert x.data_ptr() % 16 != 0
+            sl = torch.as_tensor(np.asarray(lens, dtype=np.int32)).cuda()
+            g.forward(x, sl, 1.0, out=out, path=path)
+            torch.cuda.synchronize()
+            ref = oracle.softmax_f64(workloads.to_storage(x_cpu), lens, 1.0, dtype)
+            check_against_oracle(workloads.to_storage(out.cpu()), ref, lens, dtype)
+
+
+@pytest.mark.parametrize("scale", [0.0, -1.25, 0.125, 3.0])
+def test_scale_values(scale):
+    for dtype in DTYPES:
+        x = workloads.scores_cpu((2, 3, 70, 70), dtype, 1.0, seed=5000)
+        check_small(x, [70, 33], scale, dtype)
+
+
+def test_long_rows_every_path():
+    """Rows of 4096 (binary16) and 8192 (bfloat16 and binary32) elements through each path
+    that can hold them, compared on whole planes."""
+    cases = [(workloads.F16, 4096, [4096, 2000], 0.125), (workloads.BF16, 8192, [8192], 0.125),
+             (workloads.F32, 8192, [5000], 1.0)]
+    for dtype, S, lens, scale in cases:
+        x = workloads.scores_cpu((len(lens), 1, S, S), dtype, 2.0, seed=6000 + S)
+        ref = oracle.softmax_f64(workloads.to_storage(x), lens, scale, dtype)
+        for path in ("auto", "wave", "block", "stream"):
+            if not path_ok(path, S, dtype):
+                continue
+            print(f"long rows S={S} dtype={DNAME[dtype]} path={path}", flush=True)
+            y = run_gpu(x, lens, scale, path)
+            check_against_oracle(workloads.to_storage(y.cpu()), ref, lens, dtype)
+
+
+def sample_rows_check(x_dev, y_dev, lens, scale, dtype, rows):
+    """Compare sampled rows (b, m, r) with the oracle's row entry point."""
+    xs = torch.stack([x_dev[b, m, r] for b, m, r in rows]).cpu()
+    ys = torch.stack([y_dev[b, m, r] for b, m, r in rows]).cpu()
+    ref = oracle.softmax_rows_f64(workloads.to_storage(xs), [r for _, _, r in rows],
+                                  [lens[b] for b, _, _ in rows], scale, dtype)
+    got = to_f64(workloads.to_storage(ys), dtype)
+    gb = bits(workloads.to_storage(ys))
+    S = x_dev.shape[-1]
+    worst = 0.0
+    for i, (b, m, r) in enumerate(rows):
+        keep = kept_mask(S, lens[b])[r]
+        assert not gb[i][~keep].any(), f"masked bits set in row {(b, m, r)}"
+        if keep.any():
+            e = float(np.max(np.abs(got[i][keep] - ref[i][keep])))
+            assert e <= TOL[dtype], f"row {(b, m, r)}: error {e:.3g}"
+            worst = max(worst, e)
+    return worst
+
+
+def test_very_long_rows_sampled():
+    """Rows beyond the block path's registers (stream path) and at its limit (block
+    path), checked on sampled rows."""
+    for dtype, S, path in ((workloads.F32, 40000, "stream"), (workloads.F32, 32768, "block"),
+                           (workloads.BF16, 65536, "block")):
+        lens = [S - 17]
+        print(f"very long rows S={S} dtype={DNAME[dtype]} path={path}", flush=True)
+        x = workloads.scores_device((1, 1, S, S), dtype, 1.0, seed=7000 + S)
+        sl = torch.as_tensor(np.asarray(lens, dtype=np.int32)).cuda()
+        y = g.forward(x, sl, 0.5, path=path)
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(S)
+        rows = [(0, 0, int(r)) for r in rng.choice(S, 24, replace=False)]
+        rows += [(0, 0, 0), (0, 0, S - 18), (0, 0, S - 17), (0, 0, S - 1)]
+        sample_rows_check(x, y, lens, 0.5, dtype, rows)
+        del x, y
+        torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------------ properties
+
+def test_options_give_identical_bits():
+    """Pairing, block order and store policy change the schedule, not the arithmetic."""
+    for dtype in DTYPES:
+        for S, path in ((300, "wave"), (1000, "block"), (700, "stream")):
+            lens = [S, 123, 0, 1]
+            x = workloads.scores_cpu((4, 2, S, S), dtype, 1.0, seed=8000 + S)
+            base = bits(workloads.to_storage(run_gpu(x, lens, 0.9, path).cpu()))
+            for flags in (g.FLAG_NO_PAIR, g.FLAG_NO_XCD_ORDER, g.FLAG_CACHED_STORES, 7):
+                other = bits(workloads.to_storage(run_gpu(x, lens, 0.9, path, flags).cpu()))
+                assert np.array_equal(base, other), (DNAME[dtype], S, path, flags)
+
+
+def test_in_place_and_repeat_determinism():
+    for dtype in DTYPES:
+        S = 513
+        lens = [S, 200, 0]
+        x_cpu = workloads.scores_cpu((3, 2, S, S), dtype, 1.0, seed=9000)
+        ref = bits(workloads.to_storage(run_gpu(x_cpu, lens, 1.0).cpu()))
+        for _ in range(2):
+            again = bits(workloads.to_storage(run_gpu(x_cpu, lens, 1.0).cpu()))
+            assert np.array_equal(ref, again)
+        x = x_cpu.cuda()
+        sl = torch.as_tensor(np.asarray(lens, dtype=np.int32)).cuda()
+        g.forward(x, sl, 1.0, out=x)
+        torch.cuda.synchronize()
+        assert np.array_equal(ref, bits(workloads.to_storage(x.cpu())))
+
+
+def test_masked_poison_does_not_leak():
+    """NaN and infinities in every masked cell leave the output bits unchanged."""
+    for dtype in DTYPES:
+        S = 200
+        lens = [S, 77, 0]
+        x = workloads.scores_cpu((3, 2, S, S), dtype, 1.0, seed=9100)
+        ref = bits(workloads.to_storage(run_gpu(x, lens, 1.0).cpu()))
+        for poison in (float("nan"), float("inf"), float("-inf")):
+            p = x.clone()
+            for b, L in enumerate(lens):
+                keep = torch.as_tensor(kept_mask(S, L))
+                p[b][:, ~keep] = poison
+            for path in ("wave", "block", "stream"):
+                got = bits(workloads.to_storage(run_gpu(p, lens, 1.0, path).cpu()))
+                base = bits(workloads.to_storage(run_gpu(x, lens, 1.0, path).cpu()))
+                assert np.array_equal(got, base), (DNAME[dtype], poison, path)
+            assert np.array_equal(bits(workloads.to_storage(run_gpu(p, lens, 1.0).cpu())), ref)
+
+
+def test_nan_in_kept_prefix_keeps_masked_zero():
+    """A NaN among the kept scores makes that row's kept outputs NaN; its masked columns
+    and every other row are unaffected."""
+    S = 64
+    x = workloads.scores_cpu((1, 1, S, S), workloads.F32, 1.0, seed=9200)
+    x[0, 0, 40, 3] = float("nan")
+    for path in ("wave", "block", "stream"):
+        y = workloads.to_storage(run_gpu(x, [S], 1.0, path).cpu())
+        assert np.all(np.isnan(y[0, 0, 40, :41]))
+        assert not y[0, 0, 40, 41:].view(np.uint32).any()
+        assert np.all(np.isfinite(y[0, 0, :40])) and np.all(np.isfinite(y[0, 0, 41:]))
+
+
+# ------------------------------------------------------------------------ full workloads
+
+def full_workload_check(name, n_sample_rows=1500):
+    """The workload at its real size, launched as the benchmark launches it (default
+    entry point, fresh seeded input on the device): sampled rows against the oracle, and
+    on every row exact zeros in the masked region and row sums of 1."""
+    w = workloads.WORKLOADS[name]
+    lens = workloads.seq_lens(w)
+    print(f"full workload {name} lens={list(lens)}", flush=True)
+    x = workloads.scores_device(w.shape, w.dtype, w.sigma, w.x_seed)
+    sl = torch.as_tensor(lens).cuda()
+    y = g.forward(x, sl, w.scale)
+    torch.cuda.synchronize()
+    B, M, S, _ = w.shape
+    rng = np.random.default_rng(w.x_seed)
+    rows = []
+    for b in range(B):
+        L = int(min(max(lens[b], 0), S))
+        m = int(rng.integers(M))
+        for r in {0, max(L - 1, 0), min(L, S - 1), S - 1, S // 2}:
+            rows.append((b, m, r))
+    for _ in range(n_sample_rows):
+        rows.append((int(rng.integers(B)), int(rng.integers(M)), int(rng.integers(S))))
+    worst = sample_rows_check(x, y, lens, w.scale, w.dtype, rows)
+    # every row: masked region zero, kept rows sum to 1
+    sum_tol = {workloads.F32: 1e-5, workloads.F16: 4e-3, workloads.BF16: 1.6e-2}[w.dtype]
+    itype = torch.int32 if w.dtype == workloads.F32 else torch.int16
+    r_idx = torch.arange(S, device="cuda")
+    upper = r_idx[None, :] > r_idx[:, None]
+    for b in range(B):
+        L = int(min(max(lens[b], 0), S))
+        masked = upper.clone()
+        masked[L:] = True
+        for m in range(M):
+            plane = y[b, m]
+            assert not (plane.view(itype)[masked] != 0).any(), (name, b, m)
+            if L:
+                sums = plane[:L].double().sum(dim=1)
+                assert float((sums - 1).abs().max()) <= sum_tol, (name, b, m)
+    print(f"{name}: worst sampled error {worst:.3g}", flush=True)
+    del x, y
+    torch.cuda.empty_cache()
+
+
+def test_full_readme_f32_3x64x1000():
+    full_workload_check("readme_f32_3x64x1000")
+
+
+def test_full_readme_f32_12x64x1000():
+    full_workload_check("readme_f32_12x64x1000")
+
+
+def test_full_scaled_f16_32x1x4096():
+    full_workload_check("scaled_f16_32x1x4096")
+
+
+def test_full_skewed_bf16_8x32x8192():
+    full_workload_check("skewed_bf16_8x32x8192", n_sample_rows=800)

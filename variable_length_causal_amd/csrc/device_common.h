@@ -1,0 +1,208 @@
+// Device-side building blocks shared by the gtms kernels (gfx950 / CDNA4, wave64).
+//
+//  - element IO through buffer instructions: every row gets its own buffer resource whose
+//    size is the number of bytes the kernel may touch, so the hardware range check turns
+//    loads past the kept prefix into zeros that fetch nothing, and drops stores past the
+//    row end; 16-byte vectors (dwordx4) on aligned rows, single elements otherwise;
+//  - fp32 <-> binary16 / bfloat16 conversions, round-to-nearest-even;
+//  - wavefront reductions over 64 lanes: DPP butterflies inside each 16-lane row, then the
+//    gfx950 permlane16/permlane32 swaps across rows; every lane ends with the same bits;
+//  - XCD-aware block order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gtms {
+
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr int kWave = 64;
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, blocks dealt round-robin
+
+// Cache-policy bits of a buffer access on gfx950: 0 = default, 2 = non-temporal (nt).
+constexpr int kPolicyDefault = 0;
+constexpr int kPolicyStream = 2;
+
+// Raw buffer resource over [base, base + bytes): stride 0, 32-bit data format word.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// ------------------------------------------------------------------------- element IO
+// Io<DT, WIDE>: WIDE moves 16 bytes per lane per access (VEC elements); otherwise one
+// element per access. raw_t is the in-memory unit; unpack/pack convert VEC elements.
+template <int DT, bool WIDE> struct Io;
+
+struct Wide16 {
+    using raw_t = u32x4;
+    static constexpr int BYTES = 16;
+    __device__ __forceinline__ static raw_t zero() { return raw_t{0u, 0u, 0u, 0u}; }
+    template <int POL> __device__ __forceinline__ static raw_t load(rsrc_t r, int off) {
+        return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POL);
+    }
+    template <int POL> __device__ __forceinline__ static void store(rsrc_t r, int off, raw_t v) {
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, POL);
+    }
+};
+
+template <> struct Io<DT_F32, true> : Wide16 {
+    static constexpr int VEC = 4;
+    __device__ __forceinline__ static void unpack(raw_t r, float (&f)[VEC]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = __builtin_bit_cast(float, r[i]);
+    }
+    __device__ __forceinline__ static raw_t pack(const float (&f)[VEC]) {
+        raw_t r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = __builtin_bit_cast(uint32_t, f[i]);
+        return r;
+    }
+};
+
+template <> struct Io<DT_F32, false> {
+    static constexpr int VEC = 1;
+    static constexpr int BYTES = 4;
+    using raw_t = uint32_t;
+    __device__ __forceinline__ static raw_t zero() { return 0u; }
+    template <int POL> __device__ __forceinline__ static raw_t load(rsrc_t r, int off) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, POL);
+    }
+    template <int POL> __device__ __forceinline__ static void store(rsrc_t r, int off, raw_t v) {
+        __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, POL);
+    }
+    __device__ __forceinline__ static void unpack(raw_t r, float (&f)[VEC]) {
+        f[0] = __builtin_bit_cast(float, r);
+    }
+    __device__ __forceinline__ static raw_t pack(const float (&f)[VEC]) {
+        return __builtin_bit_cast(uint32_t, f[0]);
+    }
+};
+
+// binary16: hardware conversions; bfloat16: widening is a 16-bit shift, narrowing uses the
+// gfx950 round-to-nearest-even conversion.
+template <int DT> struct Cvt16 {
+    __device__ __forceinline__ static f32x2 widen(uint32_t w) {
+        if constexpr (DT == DT_F16) {
+            return __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
+        } else {
+            return f32x2{__builtin_bit_cast(float, w << 16),
+                         __builtin_bit_cast(float, w & 0xffff0000u)};
+        }
+    }
+    __device__ __forceinline__ static uint32_t narrow(float a, float b) {
+        if constexpr (DT == DT_F16) {
+            return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), f16x2));
+        } else {
+            return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
+        }
+    }
+};
+
+template <int DT> struct Io16Wide : Wide16 {
+    static constexpr int VEC = 8;
+    __device__ __forceinline__ static void unpack(raw_t r, float (&f)[VEC]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f32x2 p = Cvt16<DT>::widen(r[i]);
+            f[2 * i] = p[0];
+            f[2 * i + 1] = p[1];
+        }
+    }
+    __device__ __forceinline__ static raw_t pack(const float (&f)[VEC]) {
+        raw_t r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = Cvt16<DT>::narrow(f[2 * i], f[2 * i + 1]);
+        return r;
+    }
+};
+
+template <int DT> struct Io16Narrow {
+    static constexpr int VEC = 1;
+    static constexpr int BYTES = 2;
+    using raw_t = uint32_t;  // the element in the low 16 bits
+    __device__ __forceinline__ static raw_t zero() { return 0u; }
+    template <int POL> __device__ __forceinline__ static raw_t load(rsrc_t r, int off) {
+        return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, POL);
+    }
+    template <int POL> __device__ __forceinline__ static void store(rsrc_t r, int off, raw_t v) {
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, off, 0, POL);
+    }
+    __device__ __forceinline__ static void unpack(raw_t r, float (&f)[VEC]) {
+        f[0] = Cvt16<DT>::widen(r)[0];
+    }
+    __device__ __forceinline__ static raw_t pack(const float (&f)[VEC]) {
+        return Cvt16<DT>::narrow(f[0], 0.0f) & 0xffffu;
+    }
+};
+
+template <> struct Io<DT_F16, true> : Io16Wide<DT_F16> {};
+template <> struct Io<DT_BF16, true> : Io16Wide<DT_BF16> {};
+template <> struct Io<DT_F16, false> : Io16Narrow<DT_F16> {};
+template <> struct Io<DT_BF16, false> : Io16Narrow<DT_BF16> {};
+
+// Hides a register's value from the optimiser, so that a later pass recomputes from it
+// instead of keeping an earlier pass's fp32 temporaries alive across a reduction.
+__device__ __forceinline__ void launder(u32x4& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void launder(uint32_t& v) { asm volatile("" : "+v"(v)); }
+
+// ------------------------------------------------------------------ wave64 reductions
+template <int CTRL> __device__ __forceinline__ float dpp(float v) {
+    // every lane named by the butterfly patterns below exists, so bound_ctrl is irrelevant
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        __builtin_bit_cast(int, v), __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// (own value, value of lane ^ 16) and (own, lane ^ 32), in an order that does not matter
+// for the commutative operations below.
+__device__ __forceinline__ f32x2 swap16(float v) {
+    auto p = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v),
+                                              __builtin_bit_cast(uint32_t, v), false, false);
+    return f32x2{__builtin_bit_cast(float, p[0]), __builtin_bit_cast(float, p[1])};
+}
+__device__ __forceinline__ f32x2 swap32(float v) {
+    auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v),
+                                              __builtin_bit_cast(uint32_t, v), false, false);
+    return f32x2{__builtin_bit_cast(float, p[0]), __builtin_bit_cast(float, p[1])};
+}
+
+struct OpMax { __device__ __forceinline__ static float f(float a, float b) { return fmaxf(a, b); } };
+struct OpSum { __device__ __forceinline__ static float f(float a, float b) { return a + b; } };
+
+// Reduce over the 64 lanes of the calling wavefront (all lanes active). The result is
+// identical in every lane and is returned as a wave-uniform (scalar) value.
+template <class Op> __device__ __forceinline__ float wave_reduce(float v) {
+    v = Op::f(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]: neighbours
+    v = Op::f(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]: pairs within a quad
+    v = Op::f(v, dpp<0x141>(v));  // row_half_mirror: quads within 8 lanes
+    v = Op::f(v, dpp<0x140>(v));  // row_mirror: halves within a 16-lane row
+    const f32x2 a = swap16(v);    // rows 0<->1, 2<->3
+    v = Op::f(a[0], a[1]);
+    const f32x2 b = swap32(v);    // halves of the wave
+    v = Op::f(b[0], b[1]);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
+// ------------------------------------------------------------------ block ordering
+// Blocks are dealt to the XCDs round-robin (block i runs on XCD i % 8). Renumber them so
+// that each XCD works through one contiguous range of logical blocks: neighbouring rows,
+// which can share a cache line at a row boundary, then meet in the same L2.
+__device__ __forceinline__ uint32_t xcd_order(uint32_t bid, uint32_t nblk) {
+    const uint32_t q = nblk / kXcds, rem = nblk % kXcds;
+    const uint32_t xcd = bid % kXcds, idx = bid / kXcds;
+    return xcd * q + (xcd < rem ? xcd : rem) + idx;
+}
+
+__device__ __forceinline__ int clamp_len(int32_t raw, int S) {
+    return raw < 0 ? 0 : (raw > S ? S : raw);
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+}  // namespace gtms

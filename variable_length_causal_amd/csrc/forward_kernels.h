@@ -1,0 +1,360 @@
+// Forward kernels of the grouped tril mask softmax (gfx950).
+//
+// Operation (page "Fused grouped tril mask softmax", github aoxy/Attention-Mask-Optimization
+// README, operator-behaviour section): for plane p = b*M + m of X[B, M, S, S] and row r,
+// with L = clamp(seq_lens[b], 0, S):
+//   r <  L : y[c] = exp(s*x[c] - max) / sum_{k<=r} exp(s*x[k] - max) for c <= r, else +0
+//   r >= L : y[c] = +0 for every c
+// The mask is the predicate (c <= r < L), evaluated in registers. The README's
+// implementation notes split the work the same way: a load side that supplies the masked
+// value without reading memory and a store side that writes the zeros.
+//
+// Arithmetic: z = x * k with k = scale * log2(e), so exp is the hardware v_exp_f32 (2^z)
+// and the max subtraction happens in the log2 domain. Accumulation is fp32.
+//
+// Memory: only the kept prefix of a row is read. Its buffer resource ends at the 16-byte
+// vector that holds column r, so lanes past it get zeros from the range check without a
+// fetch, and the elements of that last vector past column r are discarded by the
+// predicate. Every row is written in full; padded rows are stores only. Writes are about
+// 85-90% of the bytes, so the kernels are shaped around streaming dwordx4 stores.
+//
+// Three kernels:
+//   fwd_wave   one wavefront per row, kept prefix held in registers (NV vectors per lane);
+//   fwd_block  one workgroup of W wavefronts per row, per-wave (max, sum) partials merged
+//              through LDS with the log-sum-exp rule of the split-KV reduction in
+//              ColossalAI's flash_decoding.py (_flash_decoding_fwd_reduce_kernel);
+//   fwd_stream one workgroup per row, two passes (online max/sum, then normalise) for rows
+//              too long for registers.
+// A work unit is one row or, by default, the pair (r, S-1-r): the pair's kept prefixes add
+// up to S+1 columns whatever r is, which evens out the read and exp work per unit.
+#pragma once
+
+#include "device_common.h"
+
+namespace gtms {
+
+enum : unsigned { F_NO_PAIR = 1u, F_NO_XCD = 2u };
+
+struct FwdArgs {
+    const void* x;
+    void* y;
+    const int32_t* seq_lens;
+    uint32_t n_units;          // work units in the launch (< 2^32, checked on the host)
+    uint32_t units_per_plane;  // S, or ceil(S/2) with pairing
+    uint32_t M;
+    int S;
+    int row_bytes;             // S * element size
+    float k;                   // scale * log2(e)
+    unsigned flags;
+};
+
+struct Unit {
+    uint32_t plane;
+    int r0, r1;  // rows of the unit; r1 < 0 when the unit is one row
+};
+
+__device__ __forceinline__ Unit decode_unit(uint32_t unit, const FwdArgs& a) {
+    Unit u;
+    u.plane = unit / a.units_per_plane;
+    u.r0 = (int)(unit - u.plane * a.units_per_plane);
+    const int partner = a.S - 1 - u.r0;
+    u.r1 = (a.flags & F_NO_PAIR) || partner == u.r0 ? -1 : partner;
+    return u;
+}
+
+__device__ __forceinline__ const char* row_ptr(const void* base, uint32_t plane, int r,
+                                               const FwdArgs& a) {
+    return (const char*)base +
+           ((uint64_t)plane * (uint64_t)a.S + (uint64_t)r) * (uint64_t)a.row_bytes;
+}
+
+// ------------------------------------------------------------ one row, NA live slots
+// A row is held by a group of threads: thread `t` owns vectors t + j*STRIDE. Only the first
+// NA slots can hold kept columns (the caller picks NA from the prefix length, so the code
+// for each NA is straight-line); the remaining NV - NA slots of the row are zeros.
+//
+// Each thread first reduces its own elements: m_t = max z, e = 2^(z - m_t), s_t = sum e,
+// keeping e in registers. The group then merges the partials as the split-KV reduction of
+// ColossalAI's flash_decoding.py does (_flash_decoding_fwd_reduce_kernel):
+//   M = max_t m_t,  S = sum_t s_t * 2^(m_t - M),  y = e * 2^(m_t - M) / S,
+// so each element costs one exp. A thread without kept columns has m_t = -inf, s_t = 0.
+template <class IO, int NA, int STRIDE>
+struct RowPart {
+    float e[NA][IO::VEC];
+    float m, s;
+
+    __device__ __forceinline__ void compute(rsrc_t in, int t, int r, float k) {
+        constexpr int VEC = IO::VEC;
+        typename IO::raw_t raw[NA];
+#pragma unroll
+        for (int j = 0; j < NA; ++j)
+            raw[j] = IO::template load<kPolicyDefault>(in, (t + j * STRIDE) * IO::BYTES);
+        m = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < NA; ++j) {
+            const int kc = r + 1 - (t + j * STRIDE) * VEC;  // kept elements in this vector
+            float f[VEC];
+            IO::unpack(raw[j], f);
+#pragma unroll
+            for (int q = 0; q < VEC; ++q) {
+                e[j][q] = q < kc ? f[q] * k : -INFINITY;
+                m = fmaxf(m, e[j][q]);
+            }
+        }
+        s = 0.0f;
+        const float mm = m == -INFINITY ? 0.0f : m;  // keeps 2^(-inf - mm) = 0 well defined
+#pragma unroll
+        for (int j = 0; j < NA; ++j) {
+#pragma unroll
+            for (int q = 0; q < VEC; ++q) {
+                e[j][q] = __builtin_amdgcn_exp2f(e[j][q] - mm);
+                s += e[j][q];
+            }
+        }
+    }
+
+    // Scale of this thread's e once the group max M and sum S are known.
+    __device__ __forceinline__ float gain(float M, float S) const {
+        return m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M) / S;
+    }
+
+    // Writes all NV slots of the row. The select keeps masked columns at +0 even when g is
+    // NaN (a NaN among the kept scores).
+    template <int NV, int POL>
+    __device__ __forceinline__ void write(rsrc_t out, int t, int r, float g) const {
+        constexpr int VEC = IO::VEC;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            typename IO::raw_t o = IO::zero();
+            if (j < NA) {
+                const int kc = r + 1 - (t + j * STRIDE) * VEC;
+                float f[VEC];
+#pragma unroll
+                for (int q = 0; q < VEC; ++q) f[q] = q < kc ? e[j][q] * g : 0.0f;
+                o = IO::pack(f);
+            }
+            IO::template store<POL>(out, (t + j * STRIDE) * IO::BYTES, o);
+        }
+    }
+};
+
+template <class IO, int NV, int STRIDE, int POL>
+__device__ __forceinline__ void write_zeros(rsrc_t out, int t) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+        IO::template store<POL>(out, (t + j * STRIDE) * IO::BYTES, IO::zero());
+}
+
+// --------------------------------------------------------------------------- fwd_wave
+template <class IO, int NV, int NA, int POL>
+__device__ __forceinline__ void wave_row_na(rsrc_t in, rsrc_t out, int r, float k, int lane) {
+    RowPart<IO, NA, kWave> p;
+    p.compute(in, lane, r, k);
+    const float M = wave_reduce<OpMax>(p.m);
+    const float S = wave_reduce<OpSum>(p.m == -INFINITY ? 0.0f : p.s * __builtin_amdgcn_exp2f(p.m - M));
+    p.template write<NV, POL>(out, lane, r, p.gain(M, S));
+}
+
+template <int DT, bool WIDE, int NV, int POL>
+__device__ __forceinline__ void wave_row(const char* xr, char* yr, int r, bool valid,
+                                         const FwdArgs& a, int lane) {
+    using IO = Io<DT, WIDE>;
+    const rsrc_t out = make_rsrc(yr, (uint32_t)a.row_bytes);
+    if (!valid) {
+        write_zeros<IO, NV, kWave, POL>(out, lane);
+        return;
+    }
+    const int nin = r / IO::VEC + 1;  // vectors holding columns 0..r
+    const rsrc_t in = make_rsrc(xr, (uint32_t)(nin * IO::BYTES));
+    const int na = (nin + kWave - 1) / kWave;  // slots per lane that hold kept columns
+    if (NV >= 1 && na <= 1) wave_row_na<IO, NV, 1, POL>(in, out, r, a.k, lane);
+    else if (NV >= 2 && na <= 2) wave_row_na<IO, NV, (NV >= 2 ? 2 : NV), POL>(in, out, r, a.k, lane);
+    else if (NV >= 4 && na <= 4) wave_row_na<IO, NV, (NV >= 4 ? 4 : NV), POL>(in, out, r, a.k, lane);
+    else if (NV >= 8 && na <= 8) wave_row_na<IO, NV, (NV >= 8 ? 8 : NV), POL>(in, out, r, a.k, lane);
+    else wave_row_na<IO, NV, NV, POL>(in, out, r, a.k, lane);
+}
+
+constexpr int kWaveBlock = 256;  // 4 wavefronts, each on its own unit
+
+template <int DT, bool WIDE, int NV, int POL>
+__global__ __launch_bounds__(kWaveBlock) void fwd_wave(FwdArgs a) {
+    constexpr int waves = kWaveBlock / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t wave = uniform(threadIdx.x / kWave);
+    const uint32_t nblk = gridDim.x;
+    const uint32_t blk = (a.flags & F_NO_XCD) ? blockIdx.x : xcd_order(blockIdx.x, nblk);
+    for (uint64_t unit = (uint64_t)blk * waves + wave; unit < a.n_units;
+         unit += (uint64_t)nblk * waves) {
+        const Unit u = decode_unit((uint32_t)unit, a);
+        const int L = clamp_len(a.seq_lens[u.plane / a.M], a.S);
+        wave_row<DT, WIDE, NV, POL>(row_ptr(a.x, u.plane, u.r0, a),
+                                    (char*)row_ptr(a.y, u.plane, u.r0, a), u.r0, u.r0 < L, a,
+                                    lane);
+        if (u.r1 >= 0)
+            wave_row<DT, WIDE, NV, POL>(row_ptr(a.x, u.plane, u.r1, a),
+                                        (char*)row_ptr(a.y, u.plane, u.r1, a), u.r1, u.r1 < L,
+                                        a, lane);
+    }
+}
+
+// -------------------------------------------------------------------------- fwd_block
+// Merge of per-wave partials (m_w, s_w), s_w = sum over the wave's kept elements of
+// 2^(z - m_w): m = max_w m_w, s = sum_w s_w * 2^(m_w - m). A wave without kept elements has
+// m_w = -inf and s_w = 0 and contributes nothing.
+template <int W>
+__device__ __forceinline__ void merge_partials(const float* pm, const float* ps, float& m,
+                                               float& s) {
+    m = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < W; ++w) m = fmaxf(m, pm[w]);
+    s = 0.0f;
+#pragma unroll
+    for (int w = 0; w < W; ++w)
+        s += pm[w] == -INFINITY ? 0.0f : ps[w] * __builtin_amdgcn_exp2f(pm[w] - m);
+}
+
+template <class IO, int NV, int NA, int W, int POL>
+__device__ __forceinline__ void block_row_na(rsrc_t in, rsrc_t out, int r, float k, float* pm,
+                                             float* ps) {
+    constexpr int T = W * kWave;
+    const int t = threadIdx.x;
+    const int wave = uniform(t / kWave);
+    RowPart<IO, NA, T> p;
+    p.compute(in, t, r, k);
+    // wave partials, then the workgroup merge through LDS
+    const float mw = wave_reduce<OpMax>(p.m);
+    const float sw = mw == -INFINITY
+                         ? 0.0f
+                         : wave_reduce<OpSum>(p.m == -INFINITY ? 0.0f : p.s * __builtin_amdgcn_exp2f(p.m - mw));
+    if ((t & (kWave - 1)) == 0) {
+        pm[wave] = mw;
+        ps[wave] = sw;
+    }
+    __syncthreads();
+    float M, S;
+    merge_partials<W>(pm, ps, M, S);
+    p.template write<NV, POL>(out, t, r, p.gain(M, S));
+}
+
+template <int DT, bool WIDE, int NV, int W, int POL>
+__device__ __forceinline__ void block_row(const char* xr, char* yr, int r, bool valid,
+                                          const FwdArgs& a, float* pm, float* ps) {
+    using IO = Io<DT, WIDE>;
+    constexpr int T = W * kWave;
+    const int t = threadIdx.x;
+    const rsrc_t out = make_rsrc(yr, (uint32_t)a.row_bytes);
+    if (!valid) {  // uniform over the workgroup
+        write_zeros<IO, NV, T, POL>(out, t);
+        return;
+    }
+    const int nin = r / IO::VEC + 1;
+    const rsrc_t in = make_rsrc(xr, (uint32_t)(nin * IO::BYTES));
+    const int na = (nin + T - 1) / T;
+    if (na <= 1) block_row_na<IO, NV, 1, W, POL>(in, out, r, a.k, pm, ps);
+    else if (NV >= 2 && na <= 2) block_row_na<IO, NV, (NV >= 2 ? 2 : NV), W, POL>(in, out, r, a.k, pm, ps);
+    else if (NV >= 4 && na <= 4) block_row_na<IO, NV, (NV >= 4 ? 4 : NV), W, POL>(in, out, r, a.k, pm, ps);
+    else if (NV >= 8 && na <= 8) block_row_na<IO, NV, (NV >= 8 ? 8 : NV), W, POL>(in, out, r, a.k, pm, ps);
+    else block_row_na<IO, NV, NV, W, POL>(in, out, r, a.k, pm, ps);
+}
+
+template <int DT, bool WIDE, int NV, int W, int POL>
+__global__ __launch_bounds__(W * kWave) void fwd_block(FwdArgs a) {
+    __shared__ float part[2][2][W];  // [row of the unit][max, sum][wave]
+    const uint32_t nblk = gridDim.x;
+    const uint32_t blk = (a.flags & F_NO_XCD) ? blockIdx.x : xcd_order(blockIdx.x, nblk);
+    for (uint64_t unit = blk; unit < a.n_units; unit += nblk) {
+        const Unit u = decode_unit((uint32_t)unit, a);
+        const int L = clamp_len(a.seq_lens[u.plane / a.M], a.S);
+        block_row<DT, WIDE, NV, W, POL>(row_ptr(a.x, u.plane, u.r0, a),
+                                        (char*)row_ptr(a.y, u.plane, u.r0, a), u.r0, u.r0 < L,
+                                        a, part[0][0], part[0][1]);
+        if (u.r1 >= 0)
+            block_row<DT, WIDE, NV, W, POL>(row_ptr(a.x, u.plane, u.r1, a),
+                                            (char*)row_ptr(a.y, u.plane, u.r1, a), u.r1,
+                                            u.r1 < L, a, part[1][0], part[1][1]);
+        __syncthreads();  // the next unit rewrites the partials
+    }
+}
+
+// ------------------------------------------------------------------------- fwd_stream
+// Two passes over a row of any length. Pass 1 keeps a running (m, s) per thread, updated
+// per vector: m' = max(m, max of the vector), s' = s * 2^(m - m') + sum 2^(z - m'); the
+// wave and workgroup merges follow the same rule. Pass 2 re-reads the prefix and writes
+// 2^(z - m) / s, then zeros.
+template <int DT, bool WIDE, int W, int POL>
+__device__ __forceinline__ void stream_row(const char* xr, char* yr, int r, bool valid,
+                                           const FwdArgs& a, float* pm, float* ps) {
+    using IO = Io<DT, WIDE>;
+    constexpr int VEC = IO::VEC;
+    constexpr int T = W * kWave;
+    const int t = threadIdx.x;
+    const int nraw = a.row_bytes / IO::BYTES;
+    const rsrc_t out = make_rsrc(yr, (uint32_t)a.row_bytes);
+    if (!valid) {
+        for (int v = t; v < nraw; v += T) IO::template store<POL>(out, v * IO::BYTES, IO::zero());
+        return;
+    }
+    const int wave = uniform(t / kWave);
+    const int nin = r / VEC + 1;
+    const rsrc_t in = make_rsrc(xr, (uint32_t)(nin * IO::BYTES));
+    float m = -INFINITY, s = 0.0f;
+    for (int v = t; v < nin; v += T) {
+        float f[VEC];
+        IO::unpack(IO::template load<kPolicyDefault>(in, v * IO::BYTES), f);
+        float vm = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            if (v * VEC + e <= r) vm = fmaxf(vm, f[e] * a.k);
+        const float mn = fmaxf(m, vm);
+        float add = 0.0f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            add += v * VEC + e <= r ? __builtin_amdgcn_exp2f(f[e] * a.k - mn) : 0.0f;
+        s = (m == -INFINITY ? 0.0f : s * __builtin_amdgcn_exp2f(m - mn)) + add;
+        m = mn;
+    }
+    const float mw = wave_reduce<OpMax>(m);
+    const float sw =
+        wave_reduce<OpSum>(m == -INFINITY ? 0.0f : s * __builtin_amdgcn_exp2f(m - mw));
+    if ((t & (kWave - 1)) == 0) {
+        pm[wave] = mw;
+        ps[wave] = sw;
+    }
+    __syncthreads();
+    float mt, st;
+    merge_partials<W>(pm, ps, mt, st);
+    const float inv = 1.0f / st;
+    for (int v = t; v < nraw; v += T) {
+        typename IO::raw_t o = IO::zero();
+        if (v < nin) {
+            float f[VEC];
+            IO::unpack(IO::template load<kPolicyDefault>(in, v * IO::BYTES), f);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                f[e] = v * VEC + e <= r ? __builtin_amdgcn_exp2f(f[e] * a.k - mt) * inv : 0.0f;
+            o = IO::pack(f);
+        }
+        IO::template store<POL>(out, v * IO::BYTES, o);
+    }
+}
+
+template <int DT, bool WIDE, int W, int POL>
+__global__ __launch_bounds__(W * kWave) void fwd_stream(FwdArgs a) {
+    __shared__ float part[2][2][W];
+    const uint32_t nblk = gridDim.x;
+    const uint32_t blk = (a.flags & F_NO_XCD) ? blockIdx.x : xcd_order(blockIdx.x, nblk);
+    for (uint64_t unit = blk; unit < a.n_units; unit += nblk) {
+        const Unit u = decode_unit((uint32_t)unit, a);
+        const int L = clamp_len(a.seq_lens[u.plane / a.M], a.S);
+        stream_row<DT, WIDE, W, POL>(row_ptr(a.x, u.plane, u.r0, a),
+                                     (char*)row_ptr(a.y, u.plane, u.r0, a), u.r0, u.r0 < L, a,
+                                     part[0][0], part[0][1]);
+        if (u.r1 >= 0)
+            stream_row<DT, WIDE, W, POL>(row_ptr(a.x, u.plane, u.r1, a),
+                                         (char*)row_ptr(a.y, u.plane, u.r1, a), u.r1, u.r1 < L,
+                                         a, part[1][0], part[1][1]);
+        __syncthreads();
+    }
+}
+
+}  // namespace gtms
