@@ -25,16 +25,21 @@ import variable_length_causal_amd as g  # noqa: E402
 
 DTYPES = [workloads.F32, workloads.F16, workloads.BF16]
 DNAME = {workloads.F32: "f32", workloads.F16: "f16", workloads.BF16: "bf16"}
-# rows each path holds in registers (elements), as in include/gtms.h
-CAP = {("wave", 4): 4096, ("wave", 2): 8192, ("block", 4): 32768, ("block", 2): 65536}
 
 
 def esize(dtype):
     return 4 if dtype == workloads.F32 else 2
 
 
-def path_ok(path, S, dtype):
-    return path in ("auto", "stream") or S <= CAP[(path, esize(dtype))]
+def path_ok(path, S, dtype, aligned=True):
+    """Whether a register-held path can take rows of S elements: a lane holds up to 16
+    vectors of 16 bytes (rows whose byte length is a multiple of 16, on an aligned
+    tensor) or 16 single elements otherwise; the block path has 8 wavefronts."""
+    if path in ("auto", "stream"):
+        return True
+    wide = aligned and (S * esize(dtype)) % 16 == 0
+    vec = 16 // esize(dtype) if wide else 1
+    return S <= 64 * vec * 16 * (8 if path == "block" else 1)
 
 
 def run_gpu(x_cpu, lens, scale, path="auto", flags=0, out=None):
@@ -78,6 +83,8 @@ def test_shape_sweep(dtype):
         x = workloads.scores_cpu((len(lens), 2, S, S), dtype, 1.5, seed=3000 + S)
         ref = oracle.softmax_f64(workloads.to_storage(x), lens, 0.7, dtype)
         for path in ("auto", "wave", "block", "stream"):
+            if not path_ok(path, S, dtype):
+                continue
             print(f"sweep S={S} dtype={DNAME[dtype]} path={path}", flush=True)
             y = run_gpu(x, lens, 0.7, path)
             check_against_oracle(workloads.to_storage(y.cpu()), ref, lens, dtype)
@@ -93,6 +100,8 @@ def test_unaligned_rows_take_the_scalar_path(dtype):
         x_cpu = workloads.scores_cpu((3, 2, S, S), dtype, 1.0, seed=4000 + S)
         n = x_cpu.numel()
         for path in ("auto", "wave", "block", "stream"):
+            if not path_ok(path, S, dtype, aligned=False):
+                continue
             buf_in = torch.zeros(n + 1, dtype=tdt, device="cuda")
             buf_out = torch.zeros(n + 1, dtype=tdt, device="cuda")
             x = buf_in[1:].view(x_cpu.shape)

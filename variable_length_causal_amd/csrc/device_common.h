@@ -6,7 +6,7 @@
 //    row end; 16-byte vectors (dwordx4) on aligned rows, single elements otherwise;
 //  - fp32 <-> binary16 / bfloat16 conversions, round-to-nearest-even;
 //  - wavefront reductions over 64 lanes: DPP butterflies inside each 16-lane row, then the
-//    gfx950 permlane16/permlane32 swaps across rows; every lane ends with the same bits;
+//    four row results combined in scalar registers; every lane ends with the same bits;
 //  - XCD-aware block order.
 #pragma once
 
@@ -56,7 +56,12 @@ template <> struct Io<DT_F32, true> : Wide16 {
     static constexpr int VEC = 4;
     __device__ __forceinline__ static void unpack(raw_t r, float (&f)[VEC]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) f[i] = __builtin_bit_cast(float, r[i]);
+        for (int i = 0; i < 4; ++i) {
+            // copy the lane out first: clang's __builtin_bit_cast of a vector element
+            // expression reads element 0 whatever the index
+            const uint32_t w = r[i];
+            f[i] = __builtin_bit_cast(float, w);
+        }
     }
     __device__ __forceinline__ static raw_t pack(const float (&f)[VEC]) {
         raw_t r;
@@ -147,11 +152,6 @@ template <> struct Io<DT_BF16, true> : Io16Wide<DT_BF16> {};
 template <> struct Io<DT_F16, false> : Io16Narrow<DT_F16> {};
 template <> struct Io<DT_BF16, false> : Io16Narrow<DT_BF16> {};
 
-// Hides a register's value from the optimiser, so that a later pass recomputes from it
-// instead of keeping an earlier pass's fp32 temporaries alive across a reduction.
-__device__ __forceinline__ void launder(u32x4& v) { asm volatile("" : "+v"(v)); }
-__device__ __forceinline__ void launder(uint32_t& v) { asm volatile("" : "+v"(v)); }
-
 // ------------------------------------------------------------------ wave64 reductions
 template <int CTRL> __device__ __forceinline__ float dpp(float v) {
     // every lane named by the butterfly patterns below exists, so bound_ctrl is irrelevant
@@ -159,34 +159,24 @@ template <int CTRL> __device__ __forceinline__ float dpp(float v) {
         __builtin_bit_cast(int, v), __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
-// (own value, value of lane ^ 16) and (own, lane ^ 32), in an order that does not matter
-// for the commutative operations below.
-__device__ __forceinline__ f32x2 swap16(float v) {
-    auto p = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v),
-                                              __builtin_bit_cast(uint32_t, v), false, false);
-    return f32x2{__builtin_bit_cast(float, p[0]), __builtin_bit_cast(float, p[1])};
-}
-__device__ __forceinline__ f32x2 swap32(float v) {
-    auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v),
-                                              __builtin_bit_cast(uint32_t, v), false, false);
-    return f32x2{__builtin_bit_cast(float, p[0]), __builtin_bit_cast(float, p[1])};
-}
-
 struct OpMax { __device__ __forceinline__ static float f(float a, float b) { return fmaxf(a, b); } };
 struct OpSum { __device__ __forceinline__ static float f(float a, float b) { return a + b; } };
 
-// Reduce over the 64 lanes of the calling wavefront (all lanes active). The result is
-// identical in every lane and is returned as a wave-uniform (scalar) value.
+// Reduce over the 64 lanes of the calling wavefront (all lanes active). DPP butterflies
+// leave every lane of a 16-lane row holding the row's result; the four row results are
+// then read into scalar registers and combined, so the value returned is wave-uniform and
+// bit-identical for every lane.
 template <class Op> __device__ __forceinline__ float wave_reduce(float v) {
     v = Op::f(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]: neighbours
     v = Op::f(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]: pairs within a quad
     v = Op::f(v, dpp<0x141>(v));  // row_half_mirror: quads within 8 lanes
     v = Op::f(v, dpp<0x140>(v));  // row_mirror: halves within a 16-lane row
-    const f32x2 a = swap16(v);    // rows 0<->1, 2<->3
-    v = Op::f(a[0], a[1]);
-    const f32x2 b = swap32(v);    // halves of the wave
-    v = Op::f(b[0], b[1]);
-    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+    const int b = __builtin_bit_cast(int, v);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+    return Op::f(Op::f(r0, r1), Op::f(r2, r3));
 }
 
 // ------------------------------------------------------------------ block ordering
