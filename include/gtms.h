@@ -66,23 +66,27 @@ enum gtms_status {
 int gtms_forward(const void* in, void* out, const int32_t* seq_lens, int64_t B, int64_t M,
                  int64_t S, float scale, int dtype, void* stream);
 
-/* Kernel choice for gtms_forward_ex. AUTO is what gtms_forward uses. */
+/* Kernel choice for gtms_forward_ex. AUTO is what gtms_forward uses. A lane holds up to
+ * 16 vectors: 16-byte vectors when the row's byte length is a multiple of 16 and both
+ * tensors are 16-byte aligned, single elements otherwise. */
 enum gtms_path {
     GTMS_PATH_AUTO = 0,
-    GTMS_PATH_WAVE = 1,   /* one 64-lane wavefront per row, the row's kept prefix held in
-                             registers (rows up to 4096 binary32 / 8192 16-bit elements) */
-    GTMS_PATH_BLOCK = 2,  /* one workgroup per row, per-wave (max, sum) partials merged
-                             through LDS (rows up to 32768 binary32 / 65536 16-bit) */
+    GTMS_PATH_WAVE = 1,   /* one 64-lane wavefront per row, the row held in registers:
+                             rows up to 1024 vectors (4096 binary32 / 8192 16-bit
+                             elements on aligned rows) */
+    GTMS_PATH_BLOCK = 2,  /* one workgroup of 2-16 wavefronts per row, per-wave (max, sum)
+                             partials merged through LDS: rows up to 16384 vectors */
     GTMS_PATH_STREAM = 3  /* one workgroup per row, two passes over the row: online
-                             (max, sum) then normalise (any row length) */
+                             (max, sum), then normalise (any row length) */
 };
 
 /* Option bits for gtms_forward_ex (0 = the defaults gtms_forward uses). */
 enum gtms_flags {
-    GTMS_FLAG_NO_PAIR = 1u << 0,     /* do not pair row r with row S-1-r in one work unit */
-    GTMS_FLAG_NO_XCD_ORDER = 1u << 1,/* plain block order instead of contiguous row ranges
-                                        per XCD */
-    GTMS_FLAG_CACHED_STORES = 1u << 2/* ordinary stores instead of non-temporal ones */
+    GTMS_FLAG_PAIR_ROWS = 1u << 0,  /* one work unit = rows r and S-1-r (equal prefix work per
+                                       unit; slower on MI355X, where adjacent rows written
+                                       together keep HBM accesses local) */
+    GTMS_FLAG_XCD_ORDER = 1u << 1   /* give each XCD one contiguous range of rows (also
+                                       measured slower) */
 };
 
 /*

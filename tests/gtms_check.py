@@ -17,6 +17,12 @@ def kept_mask(S: int, L: int) -> np.ndarray:
     return (c <= r) & (r < L)
 
 
+def kept_row(S: int, L: int, r: int) -> np.ndarray:
+    """bool [S]: the kept columns of row r (c <= r < L, L clamped to [0, S])."""
+    L = min(max(int(L), 0), S)
+    return (np.arange(S) <= r) & (r < L)
+
+
 def to_f64(storage: np.ndarray, dtype: int) -> np.ndarray:
     """Exact fp64 values of raw element storage (float32, or uint16 bits)."""
     if dtype == workloads.F32:

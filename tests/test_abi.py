@@ -72,6 +72,8 @@ def test_path_checks(lib):
         return lib.gtms_forward_ex(FAKE, FAKE * 4, FAKE * 8, 1, 1, S, 1.0, dtype, path, flags,
                                    None)
     assert ex(7) == 5 and ex(-1) == 5                    # unknown path
-    assert ex(1, S=4097, dtype=0) == 5                   # row too long for the wave path
-    assert ex(1, S=8193, dtype=1) == 5
-    assert ex(2, S=32769, dtype=0) == 5                  # ... and for the block path
+    assert ex(1, S=4100, dtype=0) == 5                   # row too long for the wave path
+    assert ex(1, S=8200, dtype=1) == 5
+    assert ex(1, S=1025, dtype=0) == 5                   # unaligned rows: one element a slot
+    assert ex(2, S=65540, dtype=0) == 5                  # ... and for the block path
+    assert ex(2, S=16385, dtype=2) == 5

@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import workloads
-from gtms_check import TOL, bits, check_against_oracle, kept_mask, to_f64
+from gtms_check import TOL, bits, check_against_oracle, kept_mask, kept_row, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -39,7 +39,7 @@ def path_ok(path, S, dtype, aligned=True):
         return True
     wide = aligned and (S * esize(dtype)) % 16 == 0
     vec = 16 // esize(dtype) if wide else 1
-    return S <= 64 * vec * 16 * (8 if path == "block" else 1)
+    return S <= 64 * vec * 16 * (16 if path == "block" else 1)
 
 
 def run_gpu(x_cpu, lens, scale, path="auto", flags=0, out=None):
@@ -149,7 +149,7 @@ def sample_rows_check(x_dev, y_dev, lens, scale, dtype, rows):
     S = x_dev.shape[-1]
     worst = 0.0
     for i, (b, m, r) in enumerate(rows):
-        keep = kept_mask(S, lens[b])[r]
+        keep = kept_row(S, lens[b], r)
         assert not gb[i][~keep].any(), f"masked bits set in row {(b, m, r)}"
         if keep.any():
             e = float(np.max(np.abs(got[i][keep] - ref[i][keep])))
@@ -161,8 +161,8 @@ def sample_rows_check(x_dev, y_dev, lens, scale, dtype, rows):
 def test_very_long_rows_sampled():
     """Rows beyond the block path's registers (stream path) and at its limit (block
     path), checked on sampled rows."""
-    for dtype, S, path in ((workloads.F32, 40000, "stream"), (workloads.F32, 32768, "block"),
-                           (workloads.BF16, 65536, "block")):
+    for dtype, S, path in ((workloads.F32, 70000, "stream"), (workloads.F32, 65536, "block"),
+                           (workloads.BF16, 100000, "auto"), (workloads.F16, 40000, "auto")):
         lens = [S - 17]
         print(f"very long rows S={S} dtype={DNAME[dtype]} path={path}", flush=True)
         x = workloads.scores_device((1, 1, S, S), dtype, 1.0, seed=7000 + S)
@@ -180,13 +180,13 @@ def test_very_long_rows_sampled():
 # ------------------------------------------------------------------------ properties
 
 def test_options_give_identical_bits():
-    """Pairing, block order and store policy change the schedule, not the arithmetic."""
+    """Row pairing and XCD block order change the schedule, not the arithmetic."""
     for dtype in DTYPES:
         for S, path in ((300, "wave"), (1000, "block"), (700, "stream")):
             lens = [S, 123, 0, 1]
             x = workloads.scores_cpu((4, 2, S, S), dtype, 1.0, seed=8000 + S)
             base = bits(workloads.to_storage(run_gpu(x, lens, 0.9, path).cpu()))
-            for flags in (g.FLAG_NO_PAIR, g.FLAG_NO_XCD_ORDER, g.FLAG_CACHED_STORES, 7):
+            for flags in (g.FLAG_PAIR_ROWS, g.FLAG_XCD_ORDER, g.FLAG_PAIR_ROWS | g.FLAG_XCD_ORDER):
                 other = bits(workloads.to_storage(run_gpu(x, lens, 0.9, path, flags).cpu()))
                 assert np.array_equal(base, other), (DNAME[dtype], S, path, flags)
 

@@ -14,7 +14,7 @@ LIB = os.path.join(PKG, "libgtms.so")
 SOURCES = [os.path.join(CSRC, "gtms_api.hip")]
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-shared",
     # keep the compiler from emitting packed fp32 arithmetic (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",

@@ -15,8 +15,10 @@
 // Memory: only the kept prefix of a row is read. Its buffer resource ends at the 16-byte
 // vector that holds column r, so lanes past it get zeros from the range check without a
 // fetch, and the elements of that last vector past column r are discarded by the
-// predicate. Every row is written in full; padded rows are stores only. Writes are about
-// 85-90% of the bytes, so the kernels are shaped around streaming dwordx4 stores.
+// predicate. Every row is written in full with non-temporal dwordx4 stores; padded rows
+// are stores only. Writes are about 85-90% of the bytes. Stores of vectors that lie wholly
+// past the prefix need no data, so they are issued right after the prefix loads and drain
+// while those loads are in flight.
 //
 // Three kernels:
 //   fwd_wave   one wavefront per row, kept prefix held in registers (NV vectors per lane);
@@ -25,22 +27,26 @@
 //              ColossalAI's flash_decoding.py (_flash_decoding_fwd_reduce_kernel);
 //   fwd_stream one workgroup per row, two passes (online max/sum, then normalise) for rows
 //              too long for registers.
-// A work unit is one row or, by default, the pair (r, S-1-r): the pair's kept prefixes add
-// up to S+1 columns whatever r is, which evens out the read and exp work per unit.
+// A work unit is one row, or optionally the pair (r, S-1-r), whose kept prefixes add up to
+// S+1 columns whatever r is. Workgroups are numbered in row order by default: the rows
+// written at any moment then sit close together in memory, which HBM rewards (measured on
+// MI355X: pairing rows, or giving each XCD its own row range, cost 5-30%).
 #pragma once
 
 #include "device_common.h"
 
 namespace gtms {
 
-enum : unsigned { F_NO_PAIR = 1u, F_NO_XCD = 2u };
+enum : unsigned { F_PAIR = 1u, F_XCD = 2u };
+
+constexpr int kStorePolicy = kPolicyStream;  // non-temporal: measured faster on MI355X
 
 struct FwdArgs {
     const void* x;
     void* y;
     const int32_t* seq_lens;
     uint32_t n_units;          // work units in the launch (< 2^32, checked on the host)
-    uint32_t units_per_plane;  // S, or ceil(S/2) with pairing
+    uint32_t units_per_plane;  // S, or ceil(S/2) when rows are paired
     uint32_t M;
     int S;
     int row_bytes;             // S * element size
@@ -58,7 +64,7 @@ __device__ __forceinline__ Unit decode_unit(uint32_t unit, const FwdArgs& a) {
     u.plane = unit / a.units_per_plane;
     u.r0 = (int)(unit - u.plane * a.units_per_plane);
     const int partner = a.S - 1 - u.r0;
-    u.r1 = (a.flags & F_NO_PAIR) || partner == u.r0 ? -1 : partner;
+    u.r1 = !(a.flags & F_PAIR) || partner == u.r0 ? -1 : partner;
     return u;
 }
 
@@ -68,10 +74,19 @@ __device__ __forceinline__ const char* row_ptr(const void* base, uint32_t plane,
            ((uint64_t)plane * (uint64_t)a.S + (uint64_t)r) * (uint64_t)a.row_bytes;
 }
 
+// Zeros into slots [FROM, TO) of a row held with stride STRIDE (slots past the row end are
+// dropped by the range check of `out`).
+template <class IO, int FROM, int TO, int STRIDE>
+__device__ __forceinline__ void write_zero_slots(rsrc_t out, int t) {
+#pragma unroll
+    for (int j = FROM; j < TO; ++j)
+        IO::template store<kStorePolicy>(out, (t + j * STRIDE) * IO::BYTES, IO::zero());
+}
+
 // ------------------------------------------------------------ one row, NA live slots
 // A row is held by a group of threads: thread `t` owns vectors t + j*STRIDE. Only the first
 // NA slots can hold kept columns (the caller picks NA from the prefix length, so the code
-// for each NA is straight-line); the remaining NV - NA slots of the row are zeros.
+// for each NA is straight-line); the caller writes the other slots as zeros.
 //
 // Each thread first reduces its own elements: m_t = max z, e = 2^(z - m_t), s_t = sum e,
 // keeping e in registers. The group then merges the partials as the split-KV reduction of
@@ -80,15 +95,18 @@ __device__ __forceinline__ const char* row_ptr(const void* base, uint32_t plane,
 // so each element costs one exp. A thread without kept columns has m_t = -inf, s_t = 0.
 template <class IO, int NA, int STRIDE>
 struct RowPart {
+    typename IO::raw_t raw[NA];
     float e[NA][IO::VEC];
     float m, s;
 
-    __device__ __forceinline__ void compute(rsrc_t in, int t, int r, float k) {
-        constexpr int VEC = IO::VEC;
-        typename IO::raw_t raw[NA];
+    __device__ __forceinline__ void load(rsrc_t in, int t) {
 #pragma unroll
         for (int j = 0; j < NA; ++j)
             raw[j] = IO::template load<kPolicyDefault>(in, (t + j * STRIDE) * IO::BYTES);
+    }
+
+    __device__ __forceinline__ void compute(int t, int r, float k) {
+        constexpr int VEC = IO::VEC;
         m = -INFINITY;
 #pragma unroll
         for (int j = 0; j < NA; ++j) {
@@ -113,87 +131,82 @@ struct RowPart {
         }
     }
 
+    // This thread's partial sum rescaled to the group max M.
+    __device__ __forceinline__ float sum_at(float M) const {
+        return m == -INFINITY ? 0.0f : s * __builtin_amdgcn_exp2f(m - M);
+    }
+
     // Scale of this thread's e once the group max M and sum S are known.
     __device__ __forceinline__ float gain(float M, float S) const {
         return m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M) / S;
     }
 
-    // Writes all NV slots of the row. The select keeps masked columns at +0 even when g is
-    // NaN (a NaN among the kept scores).
-    template <int NV, int POL>
+    // Writes slots 0..NA-1. The select keeps masked columns at +0 even when g is NaN (a
+    // NaN among the kept scores).
     __device__ __forceinline__ void write(rsrc_t out, int t, int r, float g) const {
         constexpr int VEC = IO::VEC;
 #pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            typename IO::raw_t o = IO::zero();
-            if (j < NA) {
-                const int kc = r + 1 - (t + j * STRIDE) * VEC;
-                float f[VEC];
+        for (int j = 0; j < NA; ++j) {
+            const int kc = r + 1 - (t + j * STRIDE) * VEC;
+            float f[VEC];
 #pragma unroll
-                for (int q = 0; q < VEC; ++q) f[q] = q < kc ? e[j][q] * g : 0.0f;
-                o = IO::pack(f);
-            }
-            IO::template store<POL>(out, (t + j * STRIDE) * IO::BYTES, o);
+            for (int q = 0; q < VEC; ++q) f[q] = q < kc ? e[j][q] * g : 0.0f;
+            IO::template store<kStorePolicy>(out, (t + j * STRIDE) * IO::BYTES, IO::pack(f));
         }
     }
 };
 
-template <class IO, int NV, int STRIDE, int POL>
-__device__ __forceinline__ void write_zeros(rsrc_t out, int t) {
-#pragma unroll
-    for (int j = 0; j < NV; ++j)
-        IO::template store<POL>(out, (t + j * STRIDE) * IO::BYTES, IO::zero());
+// Calls f.operator()<NA>() with NA the smallest power of two (at most NV) that covers `na`
+// live slots.
+template <int NV, class F>
+__device__ __forceinline__ void with_live_slots(int na, F&& f) {
+    if (na <= 1) f.template operator()<1>();
+    else if (NV >= 2 && na <= 2) f.template operator()<(NV >= 2 ? 2 : 1)>();
+    else if (NV >= 4 && na <= 4) f.template operator()<(NV >= 4 ? 4 : 1)>();
+    else if (NV >= 8 && na <= 8) f.template operator()<(NV >= 8 ? 8 : 1)>();
+    else f.template operator()<NV>();
 }
 
 // --------------------------------------------------------------------------- fwd_wave
-template <class IO, int NV, int NA, int POL>
-__device__ __forceinline__ void wave_row_na(rsrc_t in, rsrc_t out, int r, float k, int lane) {
-    RowPart<IO, NA, kWave> p;
-    p.compute(in, lane, r, k);
-    const float M = wave_reduce<OpMax>(p.m);
-    const float S = wave_reduce<OpSum>(p.m == -INFINITY ? 0.0f : p.s * __builtin_amdgcn_exp2f(p.m - M));
-    p.template write<NV, POL>(out, lane, r, p.gain(M, S));
-}
-
-template <int DT, bool WIDE, int NV, int POL>
+template <int DT, bool WIDE, int NV>
 __device__ __forceinline__ void wave_row(const char* xr, char* yr, int r, bool valid,
                                          const FwdArgs& a, int lane) {
     using IO = Io<DT, WIDE>;
     const rsrc_t out = make_rsrc(yr, (uint32_t)a.row_bytes);
     if (!valid) {
-        write_zeros<IO, NV, kWave, POL>(out, lane);
+        write_zero_slots<IO, 0, NV, kWave>(out, lane);
         return;
     }
     const int nin = r / IO::VEC + 1;  // vectors holding columns 0..r
     const rsrc_t in = make_rsrc(xr, (uint32_t)(nin * IO::BYTES));
-    const int na = (nin + kWave - 1) / kWave;  // slots per lane that hold kept columns
-    if (NV >= 1 && na <= 1) wave_row_na<IO, NV, 1, POL>(in, out, r, a.k, lane);
-    else if (NV >= 2 && na <= 2) wave_row_na<IO, NV, (NV >= 2 ? 2 : NV), POL>(in, out, r, a.k, lane);
-    else if (NV >= 4 && na <= 4) wave_row_na<IO, NV, (NV >= 4 ? 4 : NV), POL>(in, out, r, a.k, lane);
-    else if (NV >= 8 && na <= 8) wave_row_na<IO, NV, (NV >= 8 ? 8 : NV), POL>(in, out, r, a.k, lane);
-    else wave_row_na<IO, NV, NV, POL>(in, out, r, a.k, lane);
+    with_live_slots<NV>((nin + kWave - 1) / kWave, [&]<int NA>() {
+        RowPart<IO, NA, kWave> p;
+        p.load(in, lane);
+        write_zero_slots<IO, NA, NV, kWave>(out, lane);
+        p.compute(lane, r, a.k);
+        const float M = wave_reduce<OpMax>(p.m);
+        const float S = wave_reduce<OpSum>(p.sum_at(M));
+        p.write(out, lane, r, p.gain(M, S));
+    });
 }
 
-constexpr int kWaveBlock = 256;  // 4 wavefronts, each on its own unit
-
-template <int DT, bool WIDE, int NV, int POL>
-__global__ __launch_bounds__(kWaveBlock) void fwd_wave(FwdArgs a) {
-    constexpr int waves = kWaveBlock / kWave;
+// WPB wavefronts per workgroup, each on its own unit.
+template <int DT, bool WIDE, int NV, int WPB>
+__global__ __launch_bounds__(WPB * kWave) void fwd_wave(FwdArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
-    const uint32_t wave = uniform(threadIdx.x / kWave);
+    const uint32_t wave = WPB == 1 ? 0u : (uint32_t)uniform(threadIdx.x / kWave);
     const uint32_t nblk = gridDim.x;
-    const uint32_t blk = (a.flags & F_NO_XCD) ? blockIdx.x : xcd_order(blockIdx.x, nblk);
-    for (uint64_t unit = (uint64_t)blk * waves + wave; unit < a.n_units;
-         unit += (uint64_t)nblk * waves) {
+    const uint32_t blk = (a.flags & F_XCD) ? xcd_order(blockIdx.x, nblk) : blockIdx.x;
+    for (uint64_t unit = (uint64_t)blk * WPB + wave; unit < a.n_units;
+         unit += (uint64_t)nblk * WPB) {
         const Unit u = decode_unit((uint32_t)unit, a);
         const int L = clamp_len(a.seq_lens[u.plane / a.M], a.S);
-        wave_row<DT, WIDE, NV, POL>(row_ptr(a.x, u.plane, u.r0, a),
-                                    (char*)row_ptr(a.y, u.plane, u.r0, a), u.r0, u.r0 < L, a,
-                                    lane);
+        wave_row<DT, WIDE, NV>(row_ptr(a.x, u.plane, u.r0, a),
+                               (char*)row_ptr(a.y, u.plane, u.r0, a), u.r0, u.r0 < L, a, lane);
         if (u.r1 >= 0)
-            wave_row<DT, WIDE, NV, POL>(row_ptr(a.x, u.plane, u.r1, a),
-                                        (char*)row_ptr(a.y, u.plane, u.r1, a), u.r1, u.r1 < L,
-                                        a, lane);
+            wave_row<DT, WIDE, NV>(row_ptr(a.x, u.plane, u.r1, a),
+                                   (char*)row_ptr(a.y, u.plane, u.r1, a), u.r1, u.r1 < L, a,
+                                   lane);
     }
 }
 
@@ -213,30 +226,7 @@ __device__ __forceinline__ void merge_partials(const float* pm, const float* ps,
         s += pm[w] == -INFINITY ? 0.0f : ps[w] * __builtin_amdgcn_exp2f(pm[w] - m);
 }
 
-template <class IO, int NV, int NA, int W, int POL>
-__device__ __forceinline__ void block_row_na(rsrc_t in, rsrc_t out, int r, float k, float* pm,
-                                             float* ps) {
-    constexpr int T = W * kWave;
-    const int t = threadIdx.x;
-    const int wave = uniform(t / kWave);
-    RowPart<IO, NA, T> p;
-    p.compute(in, t, r, k);
-    // wave partials, then the workgroup merge through LDS
-    const float mw = wave_reduce<OpMax>(p.m);
-    const float sw = mw == -INFINITY
-                         ? 0.0f
-                         : wave_reduce<OpSum>(p.m == -INFINITY ? 0.0f : p.s * __builtin_amdgcn_exp2f(p.m - mw));
-    if ((t & (kWave - 1)) == 0) {
-        pm[wave] = mw;
-        ps[wave] = sw;
-    }
-    __syncthreads();
-    float M, S;
-    merge_partials<W>(pm, ps, M, S);
-    p.template write<NV, POL>(out, t, r, p.gain(M, S));
-}
-
-template <int DT, bool WIDE, int NV, int W, int POL>
+template <int DT, bool WIDE, int NV, int W>
 __device__ __forceinline__ void block_row(const char* xr, char* yr, int r, bool valid,
                                           const FwdArgs& a, float* pm, float* ps) {
     using IO = Io<DT, WIDE>;
@@ -244,34 +234,46 @@ __device__ __forceinline__ void block_row(const char* xr, char* yr, int r, bool 
     const int t = threadIdx.x;
     const rsrc_t out = make_rsrc(yr, (uint32_t)a.row_bytes);
     if (!valid) {  // uniform over the workgroup
-        write_zeros<IO, NV, T, POL>(out, t);
+        write_zero_slots<IO, 0, NV, T>(out, t);
         return;
     }
+    const int wave = uniform(t / kWave);
     const int nin = r / IO::VEC + 1;
     const rsrc_t in = make_rsrc(xr, (uint32_t)(nin * IO::BYTES));
-    const int na = (nin + T - 1) / T;
-    if (na <= 1) block_row_na<IO, NV, 1, W, POL>(in, out, r, a.k, pm, ps);
-    else if (NV >= 2 && na <= 2) block_row_na<IO, NV, (NV >= 2 ? 2 : NV), W, POL>(in, out, r, a.k, pm, ps);
-    else if (NV >= 4 && na <= 4) block_row_na<IO, NV, (NV >= 4 ? 4 : NV), W, POL>(in, out, r, a.k, pm, ps);
-    else if (NV >= 8 && na <= 8) block_row_na<IO, NV, (NV >= 8 ? 8 : NV), W, POL>(in, out, r, a.k, pm, ps);
-    else block_row_na<IO, NV, NV, W, POL>(in, out, r, a.k, pm, ps);
+    with_live_slots<NV>((nin + T - 1) / T, [&]<int NA>() {
+        RowPart<IO, NA, T> p;
+        p.load(in, t);
+        write_zero_slots<IO, NA, NV, T>(out, t);
+        p.compute(t, r, a.k);
+        // wave partials, then the workgroup merge through LDS
+        const float mw = wave_reduce<OpMax>(p.m);
+        const float sw = mw == -INFINITY ? 0.0f : wave_reduce<OpSum>(p.sum_at(mw));
+        if ((t & (kWave - 1)) == 0) {
+            pm[wave] = mw;
+            ps[wave] = sw;
+        }
+        __syncthreads();
+        float M, S;
+        merge_partials<W>(pm, ps, M, S);
+        p.write(out, t, r, p.gain(M, S));
+    });
 }
 
-template <int DT, bool WIDE, int NV, int W, int POL>
+template <int DT, bool WIDE, int NV, int W>
 __global__ __launch_bounds__(W * kWave) void fwd_block(FwdArgs a) {
     __shared__ float part[2][2][W];  // [row of the unit][max, sum][wave]
     const uint32_t nblk = gridDim.x;
-    const uint32_t blk = (a.flags & F_NO_XCD) ? blockIdx.x : xcd_order(blockIdx.x, nblk);
+    const uint32_t blk = (a.flags & F_XCD) ? xcd_order(blockIdx.x, nblk) : blockIdx.x;
     for (uint64_t unit = blk; unit < a.n_units; unit += nblk) {
         const Unit u = decode_unit((uint32_t)unit, a);
         const int L = clamp_len(a.seq_lens[u.plane / a.M], a.S);
-        block_row<DT, WIDE, NV, W, POL>(row_ptr(a.x, u.plane, u.r0, a),
-                                        (char*)row_ptr(a.y, u.plane, u.r0, a), u.r0, u.r0 < L,
-                                        a, part[0][0], part[0][1]);
+        block_row<DT, WIDE, NV, W>(row_ptr(a.x, u.plane, u.r0, a),
+                                   (char*)row_ptr(a.y, u.plane, u.r0, a), u.r0, u.r0 < L, a,
+                                   part[0][0], part[0][1]);
         if (u.r1 >= 0)
-            block_row<DT, WIDE, NV, W, POL>(row_ptr(a.x, u.plane, u.r1, a),
-                                            (char*)row_ptr(a.y, u.plane, u.r1, a), u.r1,
-                                            u.r1 < L, a, part[1][0], part[1][1]);
+            block_row<DT, WIDE, NV, W>(row_ptr(a.x, u.plane, u.r1, a),
+                                       (char*)row_ptr(a.y, u.plane, u.r1, a), u.r1, u.r1 < L,
+                                       a, part[1][0], part[1][1]);
         __syncthreads();  // the next unit rewrites the partials
     }
 }
@@ -280,8 +282,8 @@ __global__ __launch_bounds__(W * kWave) void fwd_block(FwdArgs a) {
 // Two passes over a row of any length. Pass 1 keeps a running (m, s) per thread, updated
 // per vector: m' = max(m, max of the vector), s' = s * 2^(m - m') + sum 2^(z - m'); the
 // wave and workgroup merges follow the same rule. Pass 2 re-reads the prefix and writes
-// 2^(z - m) / s, then zeros.
-template <int DT, bool WIDE, int W, int POL>
+// 2^(z - m) / s. The zero tail is written first: it needs no data.
+template <int DT, bool WIDE, int W>
 __device__ __forceinline__ void stream_row(const char* xr, char* yr, int r, bool valid,
                                            const FwdArgs& a, float* pm, float* ps) {
     using IO = Io<DT, WIDE>;
@@ -291,12 +293,15 @@ __device__ __forceinline__ void stream_row(const char* xr, char* yr, int r, bool
     const int nraw = a.row_bytes / IO::BYTES;
     const rsrc_t out = make_rsrc(yr, (uint32_t)a.row_bytes);
     if (!valid) {
-        for (int v = t; v < nraw; v += T) IO::template store<POL>(out, v * IO::BYTES, IO::zero());
+        for (int v = t; v < nraw; v += T)
+            IO::template store<kStorePolicy>(out, v * IO::BYTES, IO::zero());
         return;
     }
     const int wave = uniform(t / kWave);
     const int nin = r / VEC + 1;
     const rsrc_t in = make_rsrc(xr, (uint32_t)(nin * IO::BYTES));
+    for (int v = nin + t; v < nraw; v += T)
+        IO::template store<kStorePolicy>(out, v * IO::BYTES, IO::zero());
     float m = -INFINITY, s = 0.0f;
     for (int v = t; v < nin; v += T) {
         float f[VEC];
@@ -324,35 +329,31 @@ __device__ __forceinline__ void stream_row(const char* xr, char* yr, int r, bool
     float mt, st;
     merge_partials<W>(pm, ps, mt, st);
     const float inv = 1.0f / st;
-    for (int v = t; v < nraw; v += T) {
-        typename IO::raw_t o = IO::zero();
-        if (v < nin) {
-            float f[VEC];
-            IO::unpack(IO::template load<kPolicyDefault>(in, v * IO::BYTES), f);
+    for (int v = t; v < nin; v += T) {
+        float f[VEC];
+        IO::unpack(IO::template load<kPolicyDefault>(in, v * IO::BYTES), f);
 #pragma unroll
-            for (int e = 0; e < VEC; ++e)
-                f[e] = v * VEC + e <= r ? __builtin_amdgcn_exp2f(f[e] * a.k - mt) * inv : 0.0f;
-            o = IO::pack(f);
-        }
-        IO::template store<POL>(out, v * IO::BYTES, o);
+        for (int e = 0; e < VEC; ++e)
+            f[e] = v * VEC + e <= r ? __builtin_amdgcn_exp2f(f[e] * a.k - mt) * inv : 0.0f;
+        IO::template store<kStorePolicy>(out, v * IO::BYTES, IO::pack(f));
     }
 }
 
-template <int DT, bool WIDE, int W, int POL>
+template <int DT, bool WIDE, int W>
 __global__ __launch_bounds__(W * kWave) void fwd_stream(FwdArgs a) {
     __shared__ float part[2][2][W];
     const uint32_t nblk = gridDim.x;
-    const uint32_t blk = (a.flags & F_NO_XCD) ? blockIdx.x : xcd_order(blockIdx.x, nblk);
+    const uint32_t blk = (a.flags & F_XCD) ? xcd_order(blockIdx.x, nblk) : blockIdx.x;
     for (uint64_t unit = blk; unit < a.n_units; unit += nblk) {
         const Unit u = decode_unit((uint32_t)unit, a);
         const int L = clamp_len(a.seq_lens[u.plane / a.M], a.S);
-        stream_row<DT, WIDE, W, POL>(row_ptr(a.x, u.plane, u.r0, a),
-                                     (char*)row_ptr(a.y, u.plane, u.r0, a), u.r0, u.r0 < L, a,
-                                     part[0][0], part[0][1]);
+        stream_row<DT, WIDE, W>(row_ptr(a.x, u.plane, u.r0, a),
+                                (char*)row_ptr(a.y, u.plane, u.r0, a), u.r0, u.r0 < L, a,
+                                part[0][0], part[0][1]);
         if (u.r1 >= 0)
-            stream_row<DT, WIDE, W, POL>(row_ptr(a.x, u.plane, u.r1, a),
-                                         (char*)row_ptr(a.y, u.plane, u.r1, a), u.r1, u.r1 < L,
-                                         a, part[1][0], part[1][1]);
+            stream_row<DT, WIDE, W>(row_ptr(a.x, u.plane, u.r1, a),
+                                    (char*)row_ptr(a.y, u.plane, u.r1, a), u.r1, u.r1 < L, a,
+                                    part[1][0], part[1][1]);
         __syncthreads();
     }
 }

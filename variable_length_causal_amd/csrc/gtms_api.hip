@@ -10,20 +10,24 @@
 namespace gtms {
 namespace {
 
-constexpr int kMaxNV = 16;      // register-held vectors per lane, wave and block paths
-constexpr int kBlockWaves = 8;  // wavefronts per workgroup, block and stream paths
+constexpr int kMaxNV = 16;      // register-held vectors per lane
+constexpr int kAutoNV = 4;      // vectors per lane the automatic choice aims for
+constexpr int kWaveWPB = 2;     // wavefronts per workgroup on the wave path
+constexpr int kMaxW = 16;       // wavefronts per workgroup on the block path, at most
+constexpr int kStreamW = 8;     // wavefronts per workgroup on the stream path
 constexpr int64_t kMaxGrid = int64_t(1) << 22;
 
 int esize_of(int dtype) { return dtype == GTMS_F32 ? 4 : 2; }
 
-int pow2_at_least(int64_t n) {
-    int p = 1;
+int64_t pow2_at_least(int64_t n) {
+    int64_t p = 1;
     while (p < n) p <<= 1;
     return p;
 }
 
-// Shared argument checks; on success fills the element size and the byte count of one
-// [B, M, S, S] tensor.
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Shared argument checks; on success fills the byte count of one [B, M, S, S] tensor.
 int check_common(const void* a, const void* b, const int32_t* seq_lens, int64_t B, int64_t M,
                  int64_t S, int dtype, int64_t* bytes, bool* empty) {
     if (dtype != GTMS_F32 && dtype != GTMS_F16 && dtype != GTMS_BF16) return GTMS_ERR_DTYPE;
@@ -51,36 +55,44 @@ struct Plan {
     int path;  // GTMS_PATH_WAVE / BLOCK / STREAM
     bool wide;
     int nv;    // vectors per lane (wave, block)
+    int w;     // wavefronts per row (block, stream)
 };
 
-// Capacity (elements per row) of the register-held paths.
-int64_t wave_capacity(int vec) { return int64_t(kWave) * vec * kMaxNV; }
-int64_t block_capacity(int vec) { return int64_t(kWave) * kBlockWaves * vec * kMaxNV; }
-// The wave path is chosen while a lane holds at most this many vectors; longer rows go
-// to the block path, which spreads them over 8 wavefronts and keeps occupancy up.
-constexpr int kAutoWaveNV = 4;
-
+// Kernel choice. A lane holds NV vectors (16 bytes each on rows whose byte length is a
+// multiple of 16, else one element); a row takes 64 * W * VEC * NV elements.
+//   auto:   rows up to 256 vectors -> one wavefront per row (NV <= 4); longer rows -> W
+//           wavefronts per row with NV = 4 (the stores of each instruction then cover
+//           W KB of the row); W = 16 and NV up to 16 beyond that; the stream path last.
+//   forced: the named path if it can hold the row.
 int make_plan(int64_t S, int dtype, bool wide, int path, Plan* p) {
-    const int vec = wide ? 16 / esize_of(dtype) : 1;
+    const int64_t vec = wide ? 16 / esize_of(dtype) : 1;
+    const int64_t nvec = cdiv(S, vec);  // vectors per row
     p->wide = wide;
     if (path == GTMS_PATH_AUTO) {
-        if (S <= int64_t(kWave) * vec * kAutoWaveNV) path = GTMS_PATH_WAVE;
-        else if (S <= block_capacity(vec)) path = GTMS_PATH_BLOCK;
+        if (nvec <= kWave * kAutoNV) path = GTMS_PATH_WAVE;
+        else if (nvec <= int64_t(kWave) * kMaxW * kMaxNV) path = GTMS_PATH_BLOCK;
         else path = GTMS_PATH_STREAM;
     }
     p->path = path;
     switch (path) {
         case GTMS_PATH_WAVE:
-            if (S > wave_capacity(vec)) return GTMS_ERR_PATH;
-            p->nv = pow2_at_least((S + int64_t(kWave) * vec - 1) / (int64_t(kWave) * vec));
+            if (nvec > int64_t(kWave) * kMaxNV) return GTMS_ERR_PATH;
+            p->nv = (int)pow2_at_least(cdiv(nvec, kWave));
+            p->w = 1;
             return GTMS_OK;
-        case GTMS_PATH_BLOCK:
-            if (S > block_capacity(vec)) return GTMS_ERR_PATH;
-            p->nv = pow2_at_least((S + int64_t(kWave) * kBlockWaves * vec - 1) /
-                                  (int64_t(kWave) * kBlockWaves * vec));
+        case GTMS_PATH_BLOCK: {
+            int64_t w = pow2_at_least(cdiv(nvec, int64_t(kWave) * kAutoNV));
+            if (w < 2) w = 2;
+            if (w > kMaxW) w = kMaxW;
+            const int64_t nv = pow2_at_least(cdiv(nvec, int64_t(kWave) * w));
+            if (nv > kMaxNV) return GTMS_ERR_PATH;
+            p->w = (int)w;
+            p->nv = (int)nv;
             return GTMS_OK;
+        }
         case GTMS_PATH_STREAM:
             p->nv = 0;
+            p->w = kStreamW;
             return GTMS_OK;
         default:
             return GTMS_ERR_PATH;
@@ -88,52 +100,77 @@ int make_plan(int64_t S, int dtype, bool wide, int path, Plan* p) {
 }
 
 // ----------------------------------------------------------------- launch by template
-template <int DT, bool WIDE, int NV, int POL>
+unsigned grid_for(int64_t units, int64_t per_block) {
+    const int64_t blocks = cdiv(units, per_block);
+    return (unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid);
+}
+
+template <int DT, bool WIDE, int NV>
 hipError_t launch_wave(const FwdArgs& a, hipStream_t st) {
-    const int64_t waves_per_block = kWaveBlock / kWave;
-    int64_t blocks = ((int64_t)a.n_units + waves_per_block - 1) / waves_per_block;
-    if (blocks > kMaxGrid) blocks = kMaxGrid;
-    hipLaunchKernelGGL((fwd_wave<DT, WIDE, NV, POL>), dim3((unsigned)blocks), dim3(kWaveBlock),
-                       0, st, a);
+    hipLaunchKernelGGL((fwd_wave<DT, WIDE, NV, kWaveWPB>), dim3(grid_for(a.n_units, kWaveWPB)),
+                       dim3(kWaveWPB * kWave), 0, st, a);
     return hipGetLastError();
 }
 
-template <int DT, bool WIDE, int NV, int POL>
+template <int DT, bool WIDE, int NV, int W>
 hipError_t launch_block(const FwdArgs& a, hipStream_t st) {
-    const int64_t blocks = (int64_t)a.n_units < kMaxGrid ? (int64_t)a.n_units : kMaxGrid;
-    hipLaunchKernelGGL((fwd_block<DT, WIDE, NV, kBlockWaves, POL>), dim3((unsigned)blocks),
-                       dim3(kBlockWaves * kWave), 0, st, a);
+    hipLaunchKernelGGL((fwd_block<DT, WIDE, NV, W>), dim3(grid_for(a.n_units, 1)),
+                       dim3(W * kWave), 0, st, a);
     return hipGetLastError();
 }
 
-template <int DT, bool WIDE, int POL>
+template <int DT, bool WIDE>
 hipError_t launch_stream(const FwdArgs& a, hipStream_t st) {
-    const int64_t blocks = (int64_t)a.n_units < kMaxGrid ? (int64_t)a.n_units : kMaxGrid;
-    hipLaunchKernelGGL((fwd_stream<DT, WIDE, kBlockWaves, POL>), dim3((unsigned)blocks),
-                       dim3(kBlockWaves * kWave), 0, st, a);
+    hipLaunchKernelGGL((fwd_stream<DT, WIDE, kStreamW>), dim3(grid_for(a.n_units, 1)),
+                       dim3(kStreamW * kWave), 0, st, a);
     return hipGetLastError();
 }
 
-template <int DT, bool WIDE, int POL>
-hipError_t dispatch_nv(const Plan& p, const FwdArgs& a, hipStream_t st) {
-    if (p.path == GTMS_PATH_STREAM) return launch_stream<DT, WIDE, POL>(a, st);
-    const bool wave = p.path == GTMS_PATH_WAVE;
-    switch (p.nv) {
-        case 1: return wave ? launch_wave<DT, WIDE, 1, POL>(a, st) : launch_block<DT, WIDE, 1, POL>(a, st);
-        case 2: return wave ? launch_wave<DT, WIDE, 2, POL>(a, st) : launch_block<DT, WIDE, 2, POL>(a, st);
-        case 4: return wave ? launch_wave<DT, WIDE, 4, POL>(a, st) : launch_block<DT, WIDE, 4, POL>(a, st);
-        case 8: return wave ? launch_wave<DT, WIDE, 8, POL>(a, st) : launch_block<DT, WIDE, 8, POL>(a, st);
-        case 16: return wave ? launch_wave<DT, WIDE, 16, POL>(a, st) : launch_block<DT, WIDE, 16, POL>(a, st);
+template <int DT, bool WIDE, int W>
+hipError_t block_nv_small(int nv, const FwdArgs& a, hipStream_t st) {
+    switch (nv) {
+        case 1: return launch_block<DT, WIDE, 1, W>(a, st);
+        case 2: return launch_block<DT, WIDE, 2, W>(a, st);
+        case 4: return launch_block<DT, WIDE, 4, W>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
 
+template <int DT, bool WIDE>
+hipError_t dispatch_wide(const Plan& p, const FwdArgs& a, hipStream_t st) {
+    switch (p.path) {
+        case GTMS_PATH_STREAM:
+            return launch_stream<DT, WIDE>(a, st);
+        case GTMS_PATH_WAVE:
+            switch (p.nv) {
+                case 1: return launch_wave<DT, WIDE, 1>(a, st);
+                case 2: return launch_wave<DT, WIDE, 2>(a, st);
+                case 4: return launch_wave<DT, WIDE, 4>(a, st);
+                case 8: return launch_wave<DT, WIDE, 8>(a, st);
+                case 16: return launch_wave<DT, WIDE, 16>(a, st);
+                default: return hipErrorInvalidValue;
+            }
+        default:  // block
+            switch (p.w) {
+                case 2: return block_nv_small<DT, WIDE, 2>(p.nv, a, st);
+                case 4: return block_nv_small<DT, WIDE, 4>(p.nv, a, st);
+                case 8: return block_nv_small<DT, WIDE, 8>(p.nv, a, st);
+                default:
+                    switch (p.nv) {
+                        case 1: return launch_block<DT, WIDE, 1, 16>(a, st);
+                        case 2: return launch_block<DT, WIDE, 2, 16>(a, st);
+                        case 4: return launch_block<DT, WIDE, 4, 16>(a, st);
+                        case 8: return launch_block<DT, WIDE, 8, 16>(a, st);
+                        case 16: return launch_block<DT, WIDE, 16, 16>(a, st);
+                        default: return hipErrorInvalidValue;
+                    }
+            }
+    }
+}
+
 template <int DT>
-hipError_t dispatch(const Plan& p, const FwdArgs& a, bool nt, hipStream_t st) {
-    if (nt) return p.wide ? dispatch_nv<DT, true, kPolicyStream>(p, a, st)
-                          : dispatch_nv<DT, false, kPolicyStream>(p, a, st);
-    return p.wide ? dispatch_nv<DT, true, kPolicyDefault>(p, a, st)
-                  : dispatch_nv<DT, false, kPolicyDefault>(p, a, st);
+hipError_t dispatch(const Plan& p, const FwdArgs& a, hipStream_t st) {
+    return p.wide ? dispatch_wide<DT, true>(p, a, st) : dispatch_wide<DT, false>(p, a, st);
 }
 
 int forward_impl(const void* in, void* out, const int32_t* seq_lens, int64_t B, int64_t M,
@@ -160,21 +197,20 @@ int forward_impl(const void* in, void* out, const int32_t* seq_lens, int64_t B, 
     a.S = (int)S;
     a.row_bytes = (int)(S * esize_of(dtype));
     a.flags = 0;
-    if (flags & GTMS_FLAG_NO_PAIR) a.flags |= F_NO_PAIR;
-    if (flags & GTMS_FLAG_NO_XCD_ORDER) a.flags |= F_NO_XCD;
-    a.units_per_plane = (a.flags & F_NO_PAIR) ? (uint32_t)S : (uint32_t)((S + 1) / 2);
+    if (flags & GTMS_FLAG_PAIR_ROWS) a.flags |= F_PAIR;
+    if (flags & GTMS_FLAG_XCD_ORDER) a.flags |= F_XCD;
+    a.units_per_plane = (a.flags & F_PAIR) ? (uint32_t)((S + 1) / 2) : (uint32_t)S;
     const int64_t units = B * M * (int64_t)a.units_per_plane;
     if (units > (int64_t)UINT32_MAX || B * M > (int64_t)UINT32_MAX) return GTMS_ERR_INVALID_ARG;
     a.n_units = (uint32_t)units;
     a.k = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
-    const bool nt = !(flags & GTMS_FLAG_CACHED_STORES);
 
     hipStream_t hs = (hipStream_t)stream;
     hipError_t e;
     switch (dtype) {
-        case GTMS_F32: e = dispatch<DT_F32>(plan, a, nt, hs); break;
-        case GTMS_F16: e = dispatch<DT_F16>(plan, a, nt, hs); break;
-        default: e = dispatch<DT_BF16>(plan, a, nt, hs); break;
+        case GTMS_F32: e = dispatch<DT_F32>(plan, a, hs); break;
+        case GTMS_F16: e = dispatch<DT_F16>(plan, a, hs); break;
+        default: e = dispatch<DT_BF16>(plan, a, hs); break;
     }
     return e == hipSuccess ? GTMS_OK : GTMS_ERR_HIP;
 }
