@@ -73,6 +73,7 @@ def test_path_checks(lib):
                                    None)
     assert ex(7) == 5 and ex(-1) == 5                    # unknown path
     assert ex(1, S=4100, dtype=0) == 5                   # row too long for the wave path
+    assert ex(1, S=4088, dtype=0) == 5                   # ... once the line slack is added
     assert ex(1, S=8200, dtype=1) == 5
     assert ex(1, S=1025, dtype=0) == 5                   # unaligned rows: one element a slot
     assert ex(2, S=65540, dtype=0) == 5                  # ... and for the block path

@@ -8,6 +8,8 @@ every row (exact zeros, row sums).
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 import pytest
 
@@ -33,13 +35,17 @@ def esize(dtype):
 
 def path_ok(path, S, dtype, aligned=True):
     """Whether a register-held path can take rows of S elements: a lane holds up to 16
-    vectors of 16 bytes (rows whose byte length is a multiple of 16, on an aligned
-    tensor) or 16 single elements otherwise; the block path has 8 wavefronts."""
+    slots of 16 bytes (rows whose byte length is a multiple of 16, on an aligned tensor)
+    or of one element otherwise; the block path has up to 16 wavefronts. A row of 16-byte
+    slots of at least 128 bytes may also write up to (128 - gcd(bytes, 128)) / 16 slots of
+    its predecessor's last line (torch allocations are 128-byte aligned)."""
     if path in ("auto", "stream"):
         return True
-    wide = aligned and (S * esize(dtype)) % 16 == 0
+    row_bytes = S * esize(dtype)
+    wide = aligned and row_bytes % 16 == 0
     vec = 16 // esize(dtype) if wide else 1
-    return S <= 64 * vec * 16 * (16 if path == "block" else 1)
+    slack = (128 - math.gcd(row_bytes, 128)) // 16 if wide and row_bytes >= 128 else 0
+    return -(-S // vec) + slack <= 64 * 16 * (16 if path == "block" else 1)
 
 
 def run_gpu(x_cpu, lens, scale, path="auto", flags=0, out=None):

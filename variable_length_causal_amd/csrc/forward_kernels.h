@@ -37,9 +37,8 @@
 
 namespace gtms {
 
-enum : unsigned { F_PAIR = 1u, F_XCD = 2u };
+enum : unsigned { F_PAIR = 1u, F_XCD = 2u, F_LINES = 4u };
 
-constexpr int kStorePolicy = kPolicyStream;  // non-temporal: measured faster on MI355X
 
 struct FwdArgs {
     const void* x;
@@ -47,6 +46,7 @@ struct FwdArgs {
     const int32_t* seq_lens;
     uint32_t n_units;          // work units in the launch (< 2^32, checked on the host)
     uint32_t units_per_plane;  // S, or ceil(S/2) when rows are paired
+    uint32_t n_planes;         // B * M
     uint32_t M;
     int S;
     int row_bytes;             // S * element size
@@ -76,41 +76,107 @@ __device__ __forceinline__ const char* row_ptr(const void* base, uint32_t plane,
 
 // Zeros into slots [FROM, TO) of a row held with stride STRIDE (slots past the row end are
 // dropped by the range check of `out`).
-template <class IO, int FROM, int TO, int STRIDE>
+template <class IO, int FROM, int TO, int STRIDE, int SP>
 __device__ __forceinline__ void write_zero_slots(rsrc_t out, int t) {
 #pragma unroll
     for (int j = FROM; j < TO; ++j)
-        IO::template store<kStorePolicy>(out, (t + j * STRIDE) * IO::BYTES, IO::zero());
+        IO::template store<SP>(out, (t + j * STRIDE) * IO::BYTES, IO::zero());
+}
+
+// ------------------------------------------------------------------ line ownership
+// Rows of binary32 X[., ., 1000, 1000] are 4000 bytes long, so most rows start and end in
+// the middle of a 128-byte line. Two wavefronts writing the two halves of one line at
+// different times cost HBM a partial-line write each (measured on MI355X: pure stores of
+// 4000-byte rows reach 4.6 TB/s this way, 5.6 TB/s when every wavefront writes whole
+// lines). So on rows of 128 bytes or more, each boundary line is written by ONE row:
+//   - a row's tail zone (the part of its last line that lies in the row) is handed to the
+//     next row when it holds only zeros, i.e. when the row is padded or its kept prefix
+//     ends before the zone; the next row then writes the zone's zeros in front of its own
+//     data, and the whole line goes out in one store;
+//   - otherwise the row keeps its tail zone and the line is written in two parts.
+// The first row of the tensor never extends before the tensor, nor the last one after it.
+// A row that takes the zone shifts its vectors by hv = zone bytes / 16 slots, so lane t
+// slot j holds the row's natural vector t + j*STRIDE - hv (negative: the zone's zeros).
+struct Span {
+    const char* out;     // first byte this row writes
+    uint32_t out_bytes;  // bytes it writes
+    int hv;              // leading slots that belong to the previous row's tail zone
+};
+
+// Whether the last `zone` bytes of row r (valid length L) hold kept elements.
+__device__ __forceinline__ bool tail_zone_has_data(int r, int L, int S, int zone, int esize) {
+    return zone > 0 && r < L && r >= S - zone / esize;
+}
+
+template <int ESIZE>
+__device__ __forceinline__ Span row_span(const FwdArgs& a, uint32_t plane, int r, int L) {
+    Span sp;
+    const char* row = row_ptr(a.y, plane, r, a);
+    sp.out = row;
+    sp.out_bytes = (uint32_t)a.row_bytes;
+    sp.hv = 0;
+    if (!(a.flags & F_LINES)) return sp;
+    const int head = (int)((uintptr_t)row & 127);                  // previous row's tail zone
+    const int tail = (int)((uintptr_t)(row + a.row_bytes) & 127);  // this row's tail zone
+    const bool first = plane == 0 && r == 0;
+    const bool last = plane + 1 == a.n_planes && r + 1 == a.S;
+    if (head && !first) {
+        bool prev_data;
+        if (r > 0) {
+            prev_data = tail_zone_has_data(r - 1, L, a.S, head, ESIZE);
+        } else {
+            const int Lp = clamp_len(a.seq_lens[(plane - 1) / a.M], a.S);
+            prev_data = tail_zone_has_data(a.S - 1, Lp, a.S, head, ESIZE);
+        }
+        if (!prev_data) {
+            sp.out -= head;
+            sp.out_bytes += head;
+            sp.hv = head / 16;
+        }
+    }
+    if (tail && !last && !tail_zone_has_data(r, L, a.S, tail, ESIZE)) sp.out_bytes -= tail;
+    return sp;
 }
 
 // ------------------------------------------------------------ one row, NA live slots
-// A row is held by a group of threads: thread `t` owns vectors t + j*STRIDE. Only the first
-// NA slots can hold kept columns (the caller picks NA from the prefix length, so the code
-// for each NA is straight-line); the caller writes the other slots as zeros.
+// A row is held by a group of threads: thread `t` owns slots t + j*STRIDE, slot i holding
+// the row's natural vector i - hv. Only the first NA slots can hold kept columns (the
+// caller picks NA from the prefix length, so the code for each NA is straight-line); the
+// caller writes the other slots as zeros.
 //
 // Each thread first reduces its own elements: m_t = max z, e = 2^(z - m_t), s_t = sum e,
 // keeping e in registers. The group then merges the partials as the split-KV reduction of
 // ColossalAI's flash_decoding.py does (_flash_decoding_fwd_reduce_kernel):
 //   M = max_t m_t,  S = sum_t s_t * 2^(m_t - M),  y = e * 2^(m_t - M) / S,
 // so each element costs one exp. A thread without kept columns has m_t = -inf, s_t = 0.
+constexpr int kOutOfRange = (int)0x80000000u;  // an offset every buffer range check rejects
+
 template <class IO, int NA, int STRIDE>
 struct RowPart {
     typename IO::raw_t raw[NA];
     float e[NA][IO::VEC];
     float m, s;
 
-    __device__ __forceinline__ void load(rsrc_t in, int t) {
-#pragma unroll
-        for (int j = 0; j < NA; ++j)
-            raw[j] = IO::template load<kPolicyDefault>(in, (t + j * STRIDE) * IO::BYTES);
+    // kept elements of the vector in slot j: elements q < kc are kept
+    __device__ __forceinline__ static int kept_count(int t, int j, int hv, int r) {
+        const int v = t + j * STRIDE - hv;
+        return v < 0 ? 0 : r + 1 - v * IO::VEC;
     }
 
-    __device__ __forceinline__ void compute(int t, int r, float k) {
+    __device__ __forceinline__ void load(rsrc_t in, int t, int hv) {
+#pragma unroll
+        for (int j = 0; j < NA; ++j) {
+            const int v = t + j * STRIDE - hv;
+            raw[j] = IO::template load<kPolicyDefault>(in, v < 0 ? kOutOfRange : v * IO::BYTES);
+        }
+    }
+
+    __device__ __forceinline__ void compute(int t, int hv, int r, float k) {
         constexpr int VEC = IO::VEC;
         m = -INFINITY;
 #pragma unroll
         for (int j = 0; j < NA; ++j) {
-            const int kc = r + 1 - (t + j * STRIDE) * VEC;  // kept elements in this vector
+            const int kc = kept_count(t, j, hv, r);
             float f[VEC];
             IO::unpack(raw[j], f);
 #pragma unroll
@@ -143,15 +209,16 @@ struct RowPart {
 
     // Writes slots 0..NA-1. The select keeps masked columns at +0 even when g is NaN (a
     // NaN among the kept scores).
-    __device__ __forceinline__ void write(rsrc_t out, int t, int r, float g) const {
+    template <int SP>
+    __device__ __forceinline__ void write(rsrc_t out, int t, int hv, int r, float g) const {
         constexpr int VEC = IO::VEC;
 #pragma unroll
         for (int j = 0; j < NA; ++j) {
-            const int kc = r + 1 - (t + j * STRIDE) * VEC;
+            const int kc = kept_count(t, j, hv, r);
             float f[VEC];
 #pragma unroll
             for (int q = 0; q < VEC; ++q) f[q] = q < kc ? e[j][q] * g : 0.0f;
-            IO::template store<kStorePolicy>(out, (t + j * STRIDE) * IO::BYTES, IO::pack(f));
+            IO::template store<SP>(out, (t + j * STRIDE) * IO::BYTES, IO::pack(f));
         }
     }
 };
@@ -168,30 +235,32 @@ __device__ __forceinline__ void with_live_slots(int na, F&& f) {
 }
 
 // --------------------------------------------------------------------------- fwd_wave
-template <int DT, bool WIDE, int NV>
-__device__ __forceinline__ void wave_row(const char* xr, char* yr, int r, bool valid,
-                                         const FwdArgs& a, int lane) {
+template <int DT, bool WIDE, int NV, int SP>
+__device__ __forceinline__ void wave_row(const FwdArgs& a, uint32_t plane, int r, int L,
+                                         int lane) {
     using IO = Io<DT, WIDE>;
-    const rsrc_t out = make_rsrc(yr, (uint32_t)a.row_bytes);
-    if (!valid) {
-        write_zero_slots<IO, 0, NV, kWave>(out, lane);
+    const Span sp = row_span<IO::BYTES / IO::VEC>(a, plane, r, L);
+    const rsrc_t out = make_rsrc(sp.out, sp.out_bytes);
+    if (r >= L) {
+        write_zero_slots<IO, 0, NV, kWave, SP>(out, lane);
         return;
     }
-    const int nin = r / IO::VEC + 1;  // vectors holding columns 0..r
-    const rsrc_t in = make_rsrc(xr, (uint32_t)(nin * IO::BYTES));
-    with_live_slots<NV>((nin + kWave - 1) / kWave, [&]<int NA>() {
+    const int nin = r / IO::VEC + 1;  // natural vectors holding columns 0..r
+    const rsrc_t in = make_rsrc(row_ptr(a.x, plane, r, a), (uint32_t)(nin * IO::BYTES));
+    const int hv = sp.hv;
+    with_live_slots<NV>((nin + hv + kWave - 1) / kWave, [&]<int NA>() {
         RowPart<IO, NA, kWave> p;
-        p.load(in, lane);
-        write_zero_slots<IO, NA, NV, kWave>(out, lane);
-        p.compute(lane, r, a.k);
+        p.load(in, lane, hv);
+        write_zero_slots<IO, NA, NV, kWave, SP>(out, lane);
+        p.compute(lane, hv, r, a.k);
         const float M = wave_reduce<OpMax>(p.m);
         const float S = wave_reduce<OpSum>(p.sum_at(M));
-        p.write(out, lane, r, p.gain(M, S));
+        p.template write<SP>(out, lane, hv, r, p.gain(M, S));
     });
 }
 
-// WPB wavefronts per workgroup, each on its own unit.
-template <int DT, bool WIDE, int NV, int WPB>
+// WPB wavefronts per workgroup, each on its own unit (a row, or a row pair).
+template <int DT, bool WIDE, int NV, int WPB, int SP>
 __global__ __launch_bounds__(WPB * kWave) void fwd_wave(FwdArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t wave = WPB == 1 ? 0u : (uint32_t)uniform(threadIdx.x / kWave);
@@ -201,12 +270,8 @@ __global__ __launch_bounds__(WPB * kWave) void fwd_wave(FwdArgs a) {
          unit += (uint64_t)nblk * WPB) {
         const Unit u = decode_unit((uint32_t)unit, a);
         const int L = clamp_len(a.seq_lens[u.plane / a.M], a.S);
-        wave_row<DT, WIDE, NV>(row_ptr(a.x, u.plane, u.r0, a),
-                               (char*)row_ptr(a.y, u.plane, u.r0, a), u.r0, u.r0 < L, a, lane);
-        if (u.r1 >= 0)
-            wave_row<DT, WIDE, NV>(row_ptr(a.x, u.plane, u.r1, a),
-                                   (char*)row_ptr(a.y, u.plane, u.r1, a), u.r1, u.r1 < L, a,
-                                   lane);
+        wave_row<DT, WIDE, NV, SP>(a, u.plane, u.r0, L, lane);
+        if (u.r1 >= 0) wave_row<DT, WIDE, NV, SP>(a, u.plane, u.r1, L, lane);
     }
 }
 
@@ -226,25 +291,27 @@ __device__ __forceinline__ void merge_partials(const float* pm, const float* ps,
         s += pm[w] == -INFINITY ? 0.0f : ps[w] * __builtin_amdgcn_exp2f(pm[w] - m);
 }
 
-template <int DT, bool WIDE, int NV, int W>
-__device__ __forceinline__ void block_row(const char* xr, char* yr, int r, bool valid,
-                                          const FwdArgs& a, float* pm, float* ps) {
+template <int DT, bool WIDE, int NV, int W, int SP>
+__device__ __forceinline__ void block_row(const FwdArgs& a, uint32_t plane, int r, int L,
+                                          float* pm, float* ps) {
     using IO = Io<DT, WIDE>;
     constexpr int T = W * kWave;
     const int t = threadIdx.x;
-    const rsrc_t out = make_rsrc(yr, (uint32_t)a.row_bytes);
-    if (!valid) {  // uniform over the workgroup
-        write_zero_slots<IO, 0, NV, T>(out, t);
+    const Span sp = row_span<IO::BYTES / IO::VEC>(a, plane, r, L);
+    const rsrc_t out = make_rsrc(sp.out, sp.out_bytes);
+    if (r >= L) {  // uniform over the workgroup
+        write_zero_slots<IO, 0, NV, T, SP>(out, t);
         return;
     }
     const int wave = uniform(t / kWave);
     const int nin = r / IO::VEC + 1;
-    const rsrc_t in = make_rsrc(xr, (uint32_t)(nin * IO::BYTES));
-    with_live_slots<NV>((nin + T - 1) / T, [&]<int NA>() {
+    const rsrc_t in = make_rsrc(row_ptr(a.x, plane, r, a), (uint32_t)(nin * IO::BYTES));
+    const int hv = sp.hv;
+    with_live_slots<NV>((nin + hv + T - 1) / T, [&]<int NA>() {
         RowPart<IO, NA, T> p;
-        p.load(in, t);
-        write_zero_slots<IO, NA, NV, T>(out, t);
-        p.compute(t, r, a.k);
+        p.load(in, t, hv);
+        write_zero_slots<IO, NA, NV, T, SP>(out, t);
+        p.compute(t, hv, r, a.k);
         // wave partials, then the workgroup merge through LDS
         const float mw = wave_reduce<OpMax>(p.m);
         const float sw = mw == -INFINITY ? 0.0f : wave_reduce<OpSum>(p.sum_at(mw));
@@ -255,11 +322,11 @@ __device__ __forceinline__ void block_row(const char* xr, char* yr, int r, bool 
         __syncthreads();
         float M, S;
         merge_partials<W>(pm, ps, M, S);
-        p.write(out, t, r, p.gain(M, S));
+        p.template write<SP>(out, t, hv, r, p.gain(M, S));
     });
 }
 
-template <int DT, bool WIDE, int NV, int W>
+template <int DT, bool WIDE, int NV, int W, int SP>
 __global__ __launch_bounds__(W * kWave) void fwd_block(FwdArgs a) {
     __shared__ float part[2][2][W];  // [row of the unit][max, sum][wave]
     const uint32_t nblk = gridDim.x;
@@ -267,13 +334,8 @@ __global__ __launch_bounds__(W * kWave) void fwd_block(FwdArgs a) {
     for (uint64_t unit = blk; unit < a.n_units; unit += nblk) {
         const Unit u = decode_unit((uint32_t)unit, a);
         const int L = clamp_len(a.seq_lens[u.plane / a.M], a.S);
-        block_row<DT, WIDE, NV, W>(row_ptr(a.x, u.plane, u.r0, a),
-                                   (char*)row_ptr(a.y, u.plane, u.r0, a), u.r0, u.r0 < L, a,
-                                   part[0][0], part[0][1]);
-        if (u.r1 >= 0)
-            block_row<DT, WIDE, NV, W>(row_ptr(a.x, u.plane, u.r1, a),
-                                       (char*)row_ptr(a.y, u.plane, u.r1, a), u.r1, u.r1 < L,
-                                       a, part[1][0], part[1][1]);
+        block_row<DT, WIDE, NV, W, SP>(a, u.plane, u.r0, L, part[0][0], part[0][1]);
+        if (u.r1 >= 0) block_row<DT, WIDE, NV, W, SP>(a, u.plane, u.r1, L, part[1][0], part[1][1]);
         __syncthreads();  // the next unit rewrites the partials
     }
 }
@@ -283,7 +345,7 @@ __global__ __launch_bounds__(W * kWave) void fwd_block(FwdArgs a) {
 // per vector: m' = max(m, max of the vector), s' = s * 2^(m - m') + sum 2^(z - m'); the
 // wave and workgroup merges follow the same rule. Pass 2 re-reads the prefix and writes
 // 2^(z - m) / s. The zero tail is written first: it needs no data.
-template <int DT, bool WIDE, int W>
+template <int DT, bool WIDE, int W, int SP>
 __device__ __forceinline__ void stream_row(const char* xr, char* yr, int r, bool valid,
                                            const FwdArgs& a, float* pm, float* ps) {
     using IO = Io<DT, WIDE>;
@@ -294,14 +356,14 @@ __device__ __forceinline__ void stream_row(const char* xr, char* yr, int r, bool
     const rsrc_t out = make_rsrc(yr, (uint32_t)a.row_bytes);
     if (!valid) {
         for (int v = t; v < nraw; v += T)
-            IO::template store<kStorePolicy>(out, v * IO::BYTES, IO::zero());
+            IO::template store<SP>(out, v * IO::BYTES, IO::zero());
         return;
     }
     const int wave = uniform(t / kWave);
     const int nin = r / VEC + 1;
     const rsrc_t in = make_rsrc(xr, (uint32_t)(nin * IO::BYTES));
     for (int v = nin + t; v < nraw; v += T)
-        IO::template store<kStorePolicy>(out, v * IO::BYTES, IO::zero());
+        IO::template store<SP>(out, v * IO::BYTES, IO::zero());
     float m = -INFINITY, s = 0.0f;
     for (int v = t; v < nin; v += T) {
         float f[VEC];
@@ -335,11 +397,11 @@ __device__ __forceinline__ void stream_row(const char* xr, char* yr, int r, bool
 #pragma unroll
         for (int e = 0; e < VEC; ++e)
             f[e] = v * VEC + e <= r ? __builtin_amdgcn_exp2f(f[e] * a.k - mt) * inv : 0.0f;
-        IO::template store<kStorePolicy>(out, v * IO::BYTES, IO::pack(f));
+        IO::template store<SP>(out, v * IO::BYTES, IO::pack(f));
     }
 }
 
-template <int DT, bool WIDE, int W>
+template <int DT, bool WIDE, int W, int SP>
 __global__ __launch_bounds__(W * kWave) void fwd_stream(FwdArgs a) {
     __shared__ float part[2][2][W];
     const uint32_t nblk = gridDim.x;
@@ -347,11 +409,11 @@ __global__ __launch_bounds__(W * kWave) void fwd_stream(FwdArgs a) {
     for (uint64_t unit = blk; unit < a.n_units; unit += nblk) {
         const Unit u = decode_unit((uint32_t)unit, a);
         const int L = clamp_len(a.seq_lens[u.plane / a.M], a.S);
-        stream_row<DT, WIDE, W>(row_ptr(a.x, u.plane, u.r0, a),
+        stream_row<DT, WIDE, W, SP>(row_ptr(a.x, u.plane, u.r0, a),
                                 (char*)row_ptr(a.y, u.plane, u.r0, a), u.r0, u.r0 < L, a,
                                 part[0][0], part[0][1]);
         if (u.r1 >= 0)
-            stream_row<DT, WIDE, W>(row_ptr(a.x, u.plane, u.r1, a),
+            stream_row<DT, WIDE, W, SP>(row_ptr(a.x, u.plane, u.r1, a),
                                     (char*)row_ptr(a.y, u.plane, u.r1, a), u.r1, u.r1 < L, a,
                                     part[1][0], part[1][1]);
         __syncthreads();

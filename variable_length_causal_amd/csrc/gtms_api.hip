@@ -12,7 +12,7 @@ namespace {
 
 constexpr int kMaxNV = 16;      // register-held vectors per lane
 constexpr int kAutoNV = 4;      // vectors per lane the automatic choice aims for
-constexpr int kWaveWPB = 2;     // wavefronts per workgroup on the wave path
+constexpr int kWaveWPB = 4;     // wavefronts per workgroup on the wave path
 constexpr int kMaxW = 16;       // wavefronts per workgroup on the block path, at most
 constexpr int kStreamW = 8;     // wavefronts per workgroup on the stream path
 constexpr int64_t kMaxGrid = int64_t(1) << 22;
@@ -58,33 +58,49 @@ struct Plan {
     int w;     // wavefronts per row (block, stream)
 };
 
+// Leading slots a row may take over from the previous row under line ownership: rows
+// start at base + k * row_bytes, so on a 128-byte aligned tensor the previous row's tail
+// zone is a multiple of gcd(row_bytes, 128) bytes below 128.
+int64_t line_slack(bool lines, int64_t row_bytes, const void* out) {
+    if (!lines) return 0;
+    if ((uintptr_t)out % 128) return 7;
+    int64_t g = 128, b = row_bytes % 128;
+    while (b) {
+        const int64_t t = g % b;
+        g = b;
+        b = t;
+    }
+    return (128 - g) / 16;
+}
+
 // Kernel choice. A lane holds NV vectors (16 bytes each on rows whose byte length is a
-// multiple of 16, else one element); a row takes 64 * W * VEC * NV elements.
-//   auto:   rows up to 256 vectors -> one wavefront per row (NV <= 4); longer rows -> W
+// multiple of 16, else one element); a row takes 64 * W * NV slots, counting the slots it
+// may write for its predecessor (line_slack).
+//   auto:   rows up to 256 slots -> one wavefront per row (NV <= 4); longer rows -> W
 //           wavefronts per row with NV = 4 (the stores of each instruction then cover
 //           W KB of the row); W = 16 and NV up to 16 beyond that; the stream path last.
 //   forced: the named path if it can hold the row.
-int make_plan(int64_t S, int dtype, bool wide, int path, Plan* p) {
+int make_plan(int64_t S, int dtype, bool wide, int64_t slack, int path, Plan* p) {
     const int64_t vec = wide ? 16 / esize_of(dtype) : 1;
-    const int64_t nvec = cdiv(S, vec);  // vectors per row
+    const int64_t slots = cdiv(S, vec) + slack;  // vectors a row may span
     p->wide = wide;
     if (path == GTMS_PATH_AUTO) {
-        if (nvec <= kWave * kAutoNV) path = GTMS_PATH_WAVE;
-        else if (nvec <= int64_t(kWave) * kMaxW * kMaxNV) path = GTMS_PATH_BLOCK;
+        if (slots <= kWave * kAutoNV) path = GTMS_PATH_WAVE;
+        else if (slots <= int64_t(kWave) * kMaxW * kMaxNV) path = GTMS_PATH_BLOCK;
         else path = GTMS_PATH_STREAM;
     }
     p->path = path;
     switch (path) {
         case GTMS_PATH_WAVE:
-            if (nvec > int64_t(kWave) * kMaxNV) return GTMS_ERR_PATH;
-            p->nv = (int)pow2_at_least(cdiv(nvec, kWave));
+            if (slots > int64_t(kWave) * kMaxNV) return GTMS_ERR_PATH;
+            p->nv = (int)pow2_at_least(cdiv(slots, kWave));
             p->w = 1;
             return GTMS_OK;
         case GTMS_PATH_BLOCK: {
-            int64_t w = pow2_at_least(cdiv(nvec, int64_t(kWave) * kAutoNV));
+            int64_t w = pow2_at_least(cdiv(slots, int64_t(kWave) * kAutoNV));
             if (w < 2) w = 2;
             if (w > kMaxW) w = kMaxW;
-            const int64_t nv = pow2_at_least(cdiv(nvec, int64_t(kWave) * w));
+            const int64_t nv = pow2_at_least(cdiv(slots, int64_t(kWave) * w));
             if (nv > kMaxNV) return GTMS_ERR_PATH;
             p->w = (int)w;
             p->nv = (int)nv;
@@ -107,21 +123,21 @@ unsigned grid_for(int64_t units, int64_t per_block) {
 
 template <int DT, bool WIDE, int NV>
 hipError_t launch_wave(const FwdArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((fwd_wave<DT, WIDE, NV, kWaveWPB>), dim3(grid_for(a.n_units, kWaveWPB)),
-                       dim3(kWaveWPB * kWave), 0, st, a);
+    hipLaunchKernelGGL((fwd_wave<DT, WIDE, NV, kWaveWPB, kPolicyStream>),
+                       dim3(grid_for(a.n_units, kWaveWPB)), dim3(kWaveWPB * kWave), 0, st, a);
     return hipGetLastError();
 }
 
 template <int DT, bool WIDE, int NV, int W>
 hipError_t launch_block(const FwdArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((fwd_block<DT, WIDE, NV, W>), dim3(grid_for(a.n_units, 1)),
+    hipLaunchKernelGGL((fwd_block<DT, WIDE, NV, W, kPolicyStream>), dim3(grid_for(a.n_units, 1)),
                        dim3(W * kWave), 0, st, a);
     return hipGetLastError();
 }
 
 template <int DT, bool WIDE>
 hipError_t launch_stream(const FwdArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((fwd_stream<DT, WIDE, kStreamW>), dim3(grid_for(a.n_units, 1)),
+    hipLaunchKernelGGL((fwd_stream<DT, WIDE, kStreamW, kPolicyStream>), dim3(grid_for(a.n_units, 1)),
                        dim3(kStreamW * kWave), 0, st, a);
     return hipGetLastError();
 }
@@ -185,8 +201,11 @@ int forward_impl(const void* in, void* out, const int32_t* seq_lens, int64_t B, 
 
     const int vec = 16 / esize_of(dtype);
     const bool wide = S % vec == 0 && (uintptr_t)in % 16 == 0 && (uintptr_t)out % 16 == 0;
+    // whole-line writes at row boundaries (wave and block paths, rows of 16-byte vectors)
+    const int64_t row_bytes = S * esize_of(dtype);
+    const bool lines = wide && row_bytes >= 128 && path != GTMS_PATH_STREAM;
     Plan plan;
-    st = make_plan(S, dtype, wide, path, &plan);
+    st = make_plan(S, dtype, wide, line_slack(lines, row_bytes, out), path, &plan);
     if (st != GTMS_OK) return st;
 
     FwdArgs a;
@@ -199,10 +218,12 @@ int forward_impl(const void* in, void* out, const int32_t* seq_lens, int64_t B, 
     a.flags = 0;
     if (flags & GTMS_FLAG_PAIR_ROWS) a.flags |= F_PAIR;
     if (flags & GTMS_FLAG_XCD_ORDER) a.flags |= F_XCD;
+    if (lines && plan.path != GTMS_PATH_STREAM) a.flags |= F_LINES;
     a.units_per_plane = (a.flags & F_PAIR) ? (uint32_t)((S + 1) / 2) : (uint32_t)S;
     const int64_t units = B * M * (int64_t)a.units_per_plane;
     if (units > (int64_t)UINT32_MAX || B * M > (int64_t)UINT32_MAX) return GTMS_ERR_INVALID_ARG;
     a.n_units = (uint32_t)units;
+    a.n_planes = (uint32_t)(B * M);
     a.k = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
 
     hipStream_t hs = (hipStream_t)stream;
