@@ -9,7 +9,8 @@ shapes and can be measured with --workload.
 
 Prints ONE JSON line. value = effective HBM throughput over the algorithmic bytes of a
 step: the kept lower-triangle reads plus the full S*S writes,
-    bytes = esize * (sum_b M * L_b (L_b + 1) / 2 + B * M * S^2).
+    bytes = esize * (sum_b M * L_b (L_b + 1) / 2 + B * M * S^2)
+(--op backward: gtms_backward instead, reading two kept triangles, y and dy).
 The roofline object reports the same bytes over the kernel's average duration measured
 with HIP events on the launch stream, against the 8 TB/s HBM peak of the MI355X. The
 cpu_baseline object times the fp64 CPU oracle on the same workload on the host.
@@ -34,14 +35,16 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 METRIC = "ms and effective HBM GB/s (% of peak) for [B,M,S,S] masked softmax"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "variable_length_causal_amd", "csrc", f)
-                  for f in ("device_common.h", "forward_kernels.h", "gtms_api.hip")]
+                  for f in ("device_common.h", "forward_kernels.h", "backward_kernels.h",
+                            "gtms_api.hip")]
 
 
-def algorithmic_bytes(w: workloads.Workload, lens) -> int:
+def algorithmic_bytes(w: workloads.Workload, lens, op: str = "forward") -> int:
+    """Kept-triangle reads (one tensor forward, y and dy backward) plus full writes."""
     S = w.S
     reads = sum(w.M * min(max(int(L), 0), S) * (min(max(int(L), 0), S) + 1) // 2 for L in lens)
     writes = w.B * w.M * S * S
-    return w.esize * (reads + writes)
+    return w.esize * ((2 if op == "backward" else 1) * reads + writes)
 
 
 def kernel_sources_hash() -> str:
@@ -52,7 +55,7 @@ def kernel_sources_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
+def measured_traffic(key: str):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, or
     None if there is none for this workload or the kernel sources changed since."""
     try:
@@ -60,7 +63,7 @@ def measured_traffic(workload: str):
             data = json.load(f)
     except (OSError, ValueError):
         return None
-    ent = data.get(workload)
+    ent = data.get(key)
     if not ent or ent.get("kernel_sources_sha256") != kernel_sources_hash():
         return None
     return ent.get("hbm_bytes_per_launch")
@@ -105,6 +108,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="readme_f32_3x64x1000",
                     choices=sorted(k for k in workloads.WORKLOADS if "example" not in k))
+    ap.add_argument("--op", default="forward", choices=["forward", "backward"],
+                    help="the forward (the headline) or its backward")
     ap.add_argument("--path", default="auto", choices=["auto", "wave", "block", "stream"])
     ap.add_argument("--flags", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -130,19 +135,31 @@ def main():
     w = workloads.WORKLOADS[args.workload]
     lens = workloads.seq_lens(w)
     sl = torch.as_tensor(lens).to(dev)
-    step_bytes = algorithmic_bytes(w, lens)
+    step_bytes = algorithmic_bytes(w, lens, args.op)
     tensor_bytes = w.B * w.M * w.S * w.S * w.esize
 
     # rotate over enough (input, output) pairs that consecutive uses of one pair are
     # separated by far more than the 256 MB last-level cache; the inputs are resident
     # before the timed region starts
     nsets = int(min(4, max(1, (3 << 30) // tensor_bytes + 1)))
+    if args.op == "backward":  # and one upstream gradient per set
+        nsets = int(min(4, max(1, (3 << 30) // (2 * tensor_bytes) + 1)))
     xs = [workloads.scores_device(w.shape, w.dtype, w.sigma, w.x_seed + i, dev) for i in range(nsets)]
     ys = [torch.empty_like(xs[0]) for _ in range(nsets)]
+    gs = []
+    if args.op == "backward":
+        for i in range(nsets):  # y = the forward's output, dy = normal
+            g.forward(xs[i], sl, w.scale, out=ys[i])
+            gs.append(workloads.scores_device(w.shape, w.dtype, 1.0, w.x_seed + 100 + i, dev))
     torch.cuda.synchronize()
 
     def step(i):
-        g.forward(xs[i % nsets], sl, w.scale, out=ys[i % nsets], path=args.path, flags=args.flags)
+        if args.op == "backward":
+            g.backward(ys[i % nsets], gs[i % nsets], sl, w.scale, out=xs[i % nsets],
+                       path=args.path, flags=args.flags)
+        else:
+            g.forward(xs[i % nsets], sl, w.scale, out=ys[i % nsets], path=args.path,
+                      flags=args.flags)
 
     for i in range(args.warmup):
         step(i)
@@ -172,7 +189,8 @@ def main():
 
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = step_bytes / (avg_kernel_ms * 1e-3) / 1e9
-    traffic = measured_traffic(args.workload)
+    traffic = measured_traffic(args.workload if args.op == "forward" else
+                               f"{args.workload}:backward")
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -188,6 +206,7 @@ def main():
         "data": "synthetic (seeded normal scores generated on the device, seeded lengths)",
         "config": {
             "workload": w.name,
+            "op": args.op,
             "B": w.B, "M": w.M, "S": w.S,
             "seq_lens": [int(v) for v in lens],
             "scale": w.scale,
@@ -206,7 +225,7 @@ def main():
         },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.op == "forward":
         out["cpu_baseline"] = cpu_baseline(xs[0], lens, w, args.cpu_budget)
     print(json.dumps(out), flush=True)
 

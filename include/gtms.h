@@ -99,6 +99,24 @@ int gtms_forward_ex(const void* in, void* out, const int32_t* seq_lens, int64_t 
                     int64_t M, int64_t S, float scale, int dtype, int path, unsigned flags,
                     void* stream);
 
+/*
+ * Backward: dx = gradient of the forward with respect to its input, given the forward
+ * output y and the upstream gradient dy. For a kept element (r < L_b, c <= r)
+ *   dx[c] = scale * y[c] * (dy[c] - sum_{k <= r} dy[k] * y[k]),
+ * from the softmax derivative dy_i/dz_j = y_i (delta_ij - y_j) (page "ops(8) self-attention
+ * CUDA (下)", section 2.1); every other element is +0.0.
+ *   y, dy, dx [B, M, S, S] elements of `dtype`; dx may be dy itself (in place) but must
+ *             not overlap y, nor overlap dy partially (GTMS_ERR_INVALID_ARG).
+ * Arithmetic fp32, results rounded to nearest-even. Other conventions as for gtms_forward.
+ */
+int gtms_backward(const void* y, const void* dy, void* dx, const int32_t* seq_lens,
+                  int64_t B, int64_t M, int64_t S, float scale, int dtype, void* stream);
+
+/* Backward with an explicit kernel choice and options (as gtms_forward_ex). */
+int gtms_backward_ex(const void* y, const void* dy, void* dx, const int32_t* seq_lens,
+                     int64_t B, int64_t M, int64_t S, float scale, int dtype, int path,
+                     unsigned flags, void* stream);
+
 /* A static, human-readable description of a status code. */
 const char* gtms_status_string(int status);
 

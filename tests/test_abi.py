@@ -78,3 +78,18 @@ def test_path_checks(lib):
     assert ex(1, S=1025, dtype=0) == 5                   # unaligned rows: one element a slot
     assert ex(2, S=65540, dtype=0) == 5                  # ... and for the block path
     assert ex(2, S=16385, dtype=2) == 5
+
+
+def test_backward_argument_checks(lib):
+    Y, G, DX, SL = FAKE, FAKE * 4, FAKE * 16, FAKE * 64
+
+    def bwd(y=Y, g=G, dx=DX, sl=SL, B=1, M=1, S=8, dtype=0):
+        return lib.gtms_backward(y, g, dx, sl, B, M, S, 0.5, dtype, None)
+    assert bwd(dtype=5) == 2
+    assert bwd(g=0) == 1                                 # no upstream gradient
+    assert bwd(dx=Y) == 1                                # dx may not replace y
+    assert bwd(dx=Y + 64) == 1                           # ... nor overlap it
+    assert bwd(dx=G + 64) == 1                           # partial overlap with dy
+    assert bwd(g=G + 2) == 3                             # misaligned dy
+    assert bwd(B=0, y=0, g=0, dx=0, sl=0) == 0
+    assert lib.gtms_backward_ex(Y, G, DX, SL, 1, 1, 4100, 1.0, 0, 1, 0, None) == 5

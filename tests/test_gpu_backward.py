@@ -1,0 +1,154 @@
+"""GPU parity of the backward kernels against the oracle's backward.
+
+The forward output y and the upstream gradient dy are inputs of both sides: y comes from the
+oracle's rounded forward (small shapes) or a seeded uniform draw (full shapes), never from
+the GPU path. Masked elements of dx must be +0 bit for bit. Kept elements must satisfy, per
+element, the bound derived from the fp32 arithmetic (backward tolerance):
+    |dx_gpu - dx_ref| <= u * |dx_ref| + 1e-5 * scale * y_c * max_k |dy_k|
+with u = 2^-21 (binary32), 2^-10 (binary16), 2^-7 (bfloat16): the output rounding plus a
+few fp32 roundings, and the error of the fp32 dot product D (at most a few hundred terms
+per thread and a 64-lane tree) relative to max |dy|; plus half the subnormal spacing of the
+element type, the rounding floor near zero.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gtms_check import bits, kept_mask, kept_row, to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("GPU tests need a visible GPU", allow_module_level=True)
+
+import variable_length_causal_amd as g  # noqa: E402
+
+DTYPES = [workloads.F32, workloads.F16, workloads.BF16]
+DNAME = {workloads.F32: "f32", workloads.F16: "f16", workloads.BF16: "bf16"}
+U = {workloads.F32: 2.0 ** -21, workloads.F16: 2.0 ** -10, workloads.BF16: 2.0 ** -7}
+# half the spacing of the element type's subnormals: the rounding error floor near zero
+TINY = {workloads.F32: 2.0 ** -150, workloads.F16: 2.0 ** -25, workloads.BF16: 2.0 ** -134}
+
+
+def path_ok(path, S, dtype):
+    """As in test_gpu_parity: whether a register-held path can hold rows of S elements."""
+    if path in ("auto", "stream"):
+        return True
+    es = 4 if dtype == workloads.F32 else 2
+    row_bytes = S * es
+    wide = row_bytes % 16 == 0
+    vec = 16 // es if wide else 1
+    slack = (128 - math.gcd(row_bytes, 128)) // 16 if wide and row_bytes >= 128 else 0
+    return -(-S // vec) + slack <= 64 * 16 * (16 if path == "block" else 1)
+
+
+def check_rows(dx_st, ref, y_st, dy_st, lens_of_rows, rows_r, scale, dtype):
+    """Rows given as 2-D arrays [n, S] with their row index and length."""
+    got = to_f64(dx_st, dtype)
+    gb = bits(dx_st)
+    yv = to_f64(y_st, dtype)
+    gv = to_f64(dy_st, dtype)
+    S = dx_st.shape[-1]
+    for i, (L, r) in enumerate(zip(lens_of_rows, rows_r)):
+        keep = kept_row(S, L, r)
+        assert not gb[i][~keep].any(), f"masked bits set in row {i} (r={r}, L={L})"
+        if keep.any():
+            gmax = float(np.max(np.abs(gv[i][keep])))
+            bound = U[dtype] * np.abs(ref[i][keep]) + 1e-5 * abs(scale) * yv[i][keep] * gmax \
+                + TINY[dtype]
+            err = np.abs(got[i][keep] - ref[i][keep])
+            assert np.all(err <= bound), (i, r, L, float(np.max(err - bound)))
+
+
+def run_case(shape, dtype, lens, scale, path="auto", seed=0):
+    B, M, S, _ = shape
+    x = workloads.scores_cpu(shape, dtype, 1.0, seed)
+    y_st = oracle.softmax(workloads.to_storage(x), lens, scale, dtype)   # the forward, oracle
+    dy = workloads.scores_cpu(shape, dtype, 1.0, seed + 1)
+    dy_st = workloads.to_storage(dy)
+    ref = oracle.backward_f64(y_st, dy_st, lens, scale, dtype)
+    y_dev = workloads.from_storage(y_st, dtype).cuda()
+    sl = torch.as_tensor(np.asarray(lens, dtype=np.int32)).cuda()
+    print(f"backward shape={shape} dtype={DNAME[dtype]} path={path} lens={list(lens)}",
+          flush=True)
+    dx = g.backward(y_dev, dy.cuda(), sl, scale, path=path)
+    torch.cuda.synchronize()
+    dx_st = workloads.to_storage(dx.cpu())
+    n = B * M * S
+    lens_rows = np.repeat(np.asarray(lens), M * S)
+    rows_r = np.tile(np.arange(S), B * M)
+    check_rows(dx_st.reshape(n, S), ref.reshape(n, S), y_st.reshape(n, S),
+               dy_st.reshape(n, S), lens_rows, rows_r, scale, dtype)
+    return dx_st, y_dev, dy, sl
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DNAME[d])
+def test_backward_shape_sweep(dtype):
+    for S in (1, 3, 5, 8, 17, 64, 65, 200, 513, 1000, 1025):
+        lens = [S, max(1, S // 3), 0, S + 2]
+        for path in ("auto", "wave", "block", "stream"):
+            if path_ok(path, S, dtype):
+                run_case((4, 2, S, S), dtype, lens, 0.7, path, seed=100 + S)
+
+
+def test_backward_long_rows():
+    for dtype, S, lens in ((workloads.F16, 4096, [4096, 1500]), (workloads.BF16, 8192, [8000])):
+        for path in ("auto", "block", "stream"):
+            run_case((len(lens), 1, S, S), dtype, lens, 0.125, path, seed=200 + S)
+
+
+def test_backward_in_place_and_poison():
+    """dx written over dy gives the same bits; NaN in masked cells of y and dy changes
+    nothing."""
+    for dtype in DTYPES:
+        S = 300
+        lens = [S, 120, 0]
+        dx_st, y_dev, dy, sl = run_case((3, 2, S, S), dtype, lens, 1.0, seed=300)
+        dy_dev = dy.cuda()
+        g.backward(y_dev, dy_dev, sl, 1.0, out=dy_dev)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(workloads.to_storage(dy_dev.cpu())), bits(dx_st))
+        yp, gp = y_dev.clone(), dy.cuda()
+        for b, L in enumerate(lens):
+            masked = ~torch.as_tensor(kept_mask(S, L)).cuda()
+            yp[b][:, masked] = float("nan")
+            gp[b][:, masked] = float("inf")
+        dxp = g.backward(yp, gp, sl, 1.0)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(workloads.to_storage(dxp.cpu())), bits(dx_st))
+
+
+def test_backward_full_readme_shape_sampled():
+    """The binary32 3 x 64 x 1000 workload at full size: y drawn uniform in [0, 1) (the
+    backward is defined for any y), dy normal; sampled rows against the oracle."""
+    w = workloads.WORKLOADS["readme_f32_3x64x1000"]
+    lens = workloads.seq_lens(w)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4242)
+    y = torch.rand(w.shape, generator=gen, device="cuda")
+    dy = workloads.scores_device(w.shape, w.dtype, 1.0, 4243)
+    sl = torch.as_tensor(lens).cuda()
+    dx = g.backward(y, dy, sl, w.scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = [(int(rng.integers(w.B)), int(rng.integers(w.M)), int(rng.integers(w.S)))
+            for _ in range(600)]
+    rows += [(b, 0, r) for b in range(w.B) for r in (0, int(lens[b]) - 1, int(lens[b]), w.S - 1)]
+    ys = torch.stack([y[b, m, r] for b, m, r in rows]).cpu()
+    gs = torch.stack([dy[b, m, r] for b, m, r in rows]).cpu()
+    ds = torch.stack([dx[b, m, r] for b, m, r in rows]).cpu()
+    y_st, g_st = workloads.to_storage(ys), workloads.to_storage(gs)
+    ref = np.empty((len(rows), w.S))
+    for i, (b, m, r) in enumerate(rows):   # one [1, 1, S, S] plane holding only this row
+        yy = np.zeros((1, 1, w.S, w.S), dtype=np.float32)
+        gg = np.zeros((1, 1, w.S, w.S), dtype=np.float32)
+        yy[0, 0, r], gg[0, 0, r] = y_st[i], g_st[i]
+        ref[i] = oracle.backward_f64(yy, gg, [lens[b]], w.scale, w.dtype)[0, 0, r]
+    check_rows(workloads.to_storage(ds), ref, y_st, g_st, [lens[b] for b, _, _ in rows],
+               [r for _, _, r in rows], w.scale, w.dtype)

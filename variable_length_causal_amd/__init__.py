@@ -40,9 +40,10 @@ def _load():
     lib.gtms_forward.restype = i32
     lib.gtms_forward_ex.argtypes = [p, p, p, i64, i64, i64, f32, i32, i32, u32, p]
     lib.gtms_forward_ex.restype = i32
-    if hasattr(lib, "gtms_backward"):
-        lib.gtms_backward.argtypes = [p, p, p, p, i64, i64, i64, f32, i32, p]
-        lib.gtms_backward.restype = i32
+    lib.gtms_backward.argtypes = [p, p, p, p, i64, i64, i64, f32, i32, p]
+    lib.gtms_backward.restype = i32
+    lib.gtms_backward_ex.argtypes = [p, p, p, p, i64, i64, i64, f32, i32, i32, u32, p]
+    lib.gtms_backward_ex.restype = i32
     lib.gtms_status_string.argtypes = [i32]
     lib.gtms_status_string.restype = ctypes.c_char_p
     lib.gtms_version.argtypes = []
@@ -129,12 +130,10 @@ def forward(x, seq_lens, scale: float = 1.0, out=None, path: str = "auto", flags
     return out
 
 
-def backward(y, dy, seq_lens, scale: float = 1.0, out=None):
-    """Gradient with respect to the forward's input, given its output y and upstream dy."""
+def backward(y, dy, seq_lens, scale: float = 1.0, out=None, path: str = "auto", flags: int = 0):
+    """Gradient with respect to the forward's input, given its output y and the upstream
+    gradient dy (both [B, M, S, S]). ``out`` may be dy itself (in place), not y."""
     import torch
-    L = _load()
-    if not hasattr(L, "gtms_backward"):
-        raise RuntimeError("libgtms.so has no gtms_backward")
     _check_scores(y, "y")
     _check_scores(dy, "dy")
     _check_lens(seq_lens, y)
@@ -142,9 +141,18 @@ def backward(y, dy, seq_lens, scale: float = 1.0, out=None):
         raise ValueError("dy must match y in shape, dtype and device")
     if out is None:
         out = torch.empty_like(y)
+    elif out.shape != y.shape or out.dtype != y.dtype or not out.is_contiguous() \
+            or out.device != y.device:
+        raise ValueError("out must be a contiguous tensor of y's shape, dtype and device")
     B, M, S, _ = y.shape
+    L = _load()
     with torch.cuda.device(y.device):
-        st = L.gtms_backward(y.data_ptr(), dy.data_ptr(), out.data_ptr(), seq_lens.data_ptr(),
-                             B, M, S, float(scale), _dtype_code(y), _stream_of(y))
+        if path == "auto" and flags == 0:
+            st = L.gtms_backward(y.data_ptr(), dy.data_ptr(), out.data_ptr(), seq_lens.data_ptr(),
+                                 B, M, S, float(scale), _dtype_code(y), _stream_of(y))
+        else:
+            st = L.gtms_backward_ex(y.data_ptr(), dy.data_ptr(), out.data_ptr(),
+                                    seq_lens.data_ptr(), B, M, S, float(scale), _dtype_code(y),
+                                    PATHS[path], int(flags), _stream_of(y))
     _raise(st, "gtms_backward")
     return out

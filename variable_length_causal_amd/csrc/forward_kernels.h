@@ -40,9 +40,12 @@ namespace gtms {
 enum : unsigned { F_PAIR = 1u, F_XCD = 2u, F_LINES = 4u };
 
 
+// Arguments of the forward (x -> y) and backward (y = x, upstream gradient g -> dx = y)
+// kernels.
 struct FwdArgs {
     const void* x;
     void* y;
+    const void* g;             // backward only: the upstream gradient
     const int32_t* seq_lens;
     uint32_t n_units;          // work units in the launch (< 2^32, checked on the host)
     uint32_t units_per_plane;  // S, or ceil(S/2) when rows are paired
@@ -50,7 +53,7 @@ struct FwdArgs {
     uint32_t M;
     int S;
     int row_bytes;             // S * element size
-    float k;                   // scale * log2(e)
+    float k;                   // forward: scale * log2(e); backward: scale
     unsigned flags;
 };
 

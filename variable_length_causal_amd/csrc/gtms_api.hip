@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include "gtms.h"
+#include "backward_kernels.h"
 #include "forward_kernels.h"
 
 namespace gtms {
@@ -121,86 +122,110 @@ unsigned grid_for(int64_t units, int64_t per_block) {
     return (unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid);
 }
 
-template <int DT, bool WIDE, int NV>
+// OP selects the kernel family: forward (x -> y) or backward (y, g -> dx).
+enum : int { OP_FWD = 0, OP_BWD = 1 };
+
+template <int OP, int DT, bool WIDE, int NV>
 hipError_t launch_wave(const FwdArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((fwd_wave<DT, WIDE, NV, kWaveWPB, kPolicyStream>),
-                       dim3(grid_for(a.n_units, kWaveWPB)), dim3(kWaveWPB * kWave), 0, st, a);
+    const dim3 grid(grid_for(a.n_units, kWaveWPB)), block(kWaveWPB * kWave);
+    if constexpr (OP == OP_FWD)
+        hipLaunchKernelGGL((fwd_wave<DT, WIDE, NV, kWaveWPB, kPolicyStream>), grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL((bwd_wave<DT, WIDE, NV, kWaveWPB, kPolicyStream>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 
-template <int DT, bool WIDE, int NV, int W>
+template <int OP, int DT, bool WIDE, int NV, int W>
 hipError_t launch_block(const FwdArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((fwd_block<DT, WIDE, NV, W, kPolicyStream>), dim3(grid_for(a.n_units, 1)),
-                       dim3(W * kWave), 0, st, a);
+    const dim3 grid(grid_for(a.n_units, 1)), block(W * kWave);
+    if constexpr (OP == OP_FWD)
+        hipLaunchKernelGGL((fwd_block<DT, WIDE, NV, W, kPolicyStream>), grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL((bwd_block<DT, WIDE, NV, W, kPolicyStream>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 
-template <int DT, bool WIDE>
+template <int OP, int DT, bool WIDE>
 hipError_t launch_stream(const FwdArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((fwd_stream<DT, WIDE, kStreamW, kPolicyStream>), dim3(grid_for(a.n_units, 1)),
-                       dim3(kStreamW * kWave), 0, st, a);
+    const dim3 grid(grid_for(a.n_units, 1)), block(kStreamW * kWave);
+    if constexpr (OP == OP_FWD)
+        hipLaunchKernelGGL((fwd_stream<DT, WIDE, kStreamW, kPolicyStream>), grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL((bwd_stream<DT, WIDE, kStreamW, kPolicyStream>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 
-template <int DT, bool WIDE, int W>
+template <int OP, int DT, bool WIDE, int W>
 hipError_t block_nv_small(int nv, const FwdArgs& a, hipStream_t st) {
     switch (nv) {
-        case 1: return launch_block<DT, WIDE, 1, W>(a, st);
-        case 2: return launch_block<DT, WIDE, 2, W>(a, st);
-        case 4: return launch_block<DT, WIDE, 4, W>(a, st);
+        case 1: return launch_block<OP, DT, WIDE, 1, W>(a, st);
+        case 2: return launch_block<OP, DT, WIDE, 2, W>(a, st);
+        case 4: return launch_block<OP, DT, WIDE, 4, W>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <int DT, bool WIDE>
+template <int OP, int DT, bool WIDE>
 hipError_t dispatch_wide(const Plan& p, const FwdArgs& a, hipStream_t st) {
     switch (p.path) {
         case GTMS_PATH_STREAM:
-            return launch_stream<DT, WIDE>(a, st);
+            return launch_stream<OP, DT, WIDE>(a, st);
         case GTMS_PATH_WAVE:
             switch (p.nv) {
-                case 1: return launch_wave<DT, WIDE, 1>(a, st);
-                case 2: return launch_wave<DT, WIDE, 2>(a, st);
-                case 4: return launch_wave<DT, WIDE, 4>(a, st);
-                case 8: return launch_wave<DT, WIDE, 8>(a, st);
-                case 16: return launch_wave<DT, WIDE, 16>(a, st);
+                case 1: return launch_wave<OP, DT, WIDE, 1>(a, st);
+                case 2: return launch_wave<OP, DT, WIDE, 2>(a, st);
+                case 4: return launch_wave<OP, DT, WIDE, 4>(a, st);
+                case 8: return launch_wave<OP, DT, WIDE, 8>(a, st);
+                case 16: return launch_wave<OP, DT, WIDE, 16>(a, st);
                 default: return hipErrorInvalidValue;
             }
         default:  // block
             switch (p.w) {
-                case 2: return block_nv_small<DT, WIDE, 2>(p.nv, a, st);
-                case 4: return block_nv_small<DT, WIDE, 4>(p.nv, a, st);
-                case 8: return block_nv_small<DT, WIDE, 8>(p.nv, a, st);
+                case 2: return block_nv_small<OP, DT, WIDE, 2>(p.nv, a, st);
+                case 4: return block_nv_small<OP, DT, WIDE, 4>(p.nv, a, st);
+                case 8: return block_nv_small<OP, DT, WIDE, 8>(p.nv, a, st);
                 default:
                     switch (p.nv) {
-                        case 1: return launch_block<DT, WIDE, 1, 16>(a, st);
-                        case 2: return launch_block<DT, WIDE, 2, 16>(a, st);
-                        case 4: return launch_block<DT, WIDE, 4, 16>(a, st);
-                        case 8: return launch_block<DT, WIDE, 8, 16>(a, st);
-                        case 16: return launch_block<DT, WIDE, 16, 16>(a, st);
+                        case 1: return launch_block<OP, DT, WIDE, 1, 16>(a, st);
+                        case 2: return launch_block<OP, DT, WIDE, 2, 16>(a, st);
+                        case 4: return launch_block<OP, DT, WIDE, 4, 16>(a, st);
+                        case 8: return launch_block<OP, DT, WIDE, 8, 16>(a, st);
+                        case 16: return launch_block<OP, DT, WIDE, 16, 16>(a, st);
                         default: return hipErrorInvalidValue;
                     }
             }
     }
 }
 
-template <int DT>
+template <int OP, int DT>
 hipError_t dispatch(const Plan& p, const FwdArgs& a, hipStream_t st) {
-    return p.wide ? dispatch_wide<DT, true>(p, a, st) : dispatch_wide<DT, false>(p, a, st);
+    return p.wide ? dispatch_wide<OP, DT, true>(p, a, st) : dispatch_wide<OP, DT, false>(p, a, st);
 }
 
-int forward_impl(const void* in, void* out, const int32_t* seq_lens, int64_t B, int64_t M,
-                 int64_t S, float scale, int dtype, int path, unsigned flags, void* stream) {
+// Shared body of the forward (x -> out) and backward (x = y, g = dy -> out = dx) calls.
+template <int OP>
+int run_impl(const void* x, const void* g, void* out, const int32_t* seq_lens, int64_t B,
+             int64_t M, int64_t S, float scale, int dtype, int path, unsigned flags,
+             void* stream) {
     int64_t bytes;
     bool empty;
-    int st = check_common(in, out, seq_lens, B, M, S, dtype, &bytes, &empty);
+    int st = check_common(x, out, seq_lens, B, M, S, dtype, &bytes, &empty);
     if (st != GTMS_OK) return st;
     if (path < GTMS_PATH_AUTO || path > GTMS_PATH_STREAM) return GTMS_ERR_PATH;
     if (empty) return GTMS_OK;
-    if (overlap_partial(in, out, bytes)) return GTMS_ERR_INVALID_ARG;
+    if (OP == OP_BWD) {
+        if (!g) return GTMS_ERR_INVALID_ARG;
+        if ((uintptr_t)g % esize_of(dtype)) return GTMS_ERR_ALIGN;
+        // dx may replace dy, but must not touch y or overlap dy partially
+        if (overlap_partial(g, out, bytes) || overlap_partial(x, out, bytes) || x == out)
+            return GTMS_ERR_INVALID_ARG;
+    } else if (overlap_partial(x, out, bytes)) {
+        return GTMS_ERR_INVALID_ARG;
+    }
 
     const int vec = 16 / esize_of(dtype);
-    const bool wide = S % vec == 0 && (uintptr_t)in % 16 == 0 && (uintptr_t)out % 16 == 0;
+    const bool wide = S % vec == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)out % 16 == 0 &&
+                      (OP == OP_FWD || (uintptr_t)g % 16 == 0);
     // whole-line writes at row boundaries (wave and block paths, rows of 16-byte vectors)
     const int64_t row_bytes = S * esize_of(dtype);
     const bool lines = wide && row_bytes >= 128 && path != GTMS_PATH_STREAM;
@@ -209,12 +234,13 @@ int forward_impl(const void* in, void* out, const int32_t* seq_lens, int64_t B, 
     if (st != GTMS_OK) return st;
 
     FwdArgs a;
-    a.x = in;
+    a.x = x;
     a.y = out;
+    a.g = g;
     a.seq_lens = seq_lens;
     a.M = (uint32_t)M;
     a.S = (int)S;
-    a.row_bytes = (int)(S * esize_of(dtype));
+    a.row_bytes = (int)row_bytes;
     a.flags = 0;
     if (flags & GTMS_FLAG_PAIR_ROWS) a.flags |= F_PAIR;
     if (flags & GTMS_FLAG_XCD_ORDER) a.flags |= F_XCD;
@@ -224,14 +250,15 @@ int forward_impl(const void* in, void* out, const int32_t* seq_lens, int64_t B, 
     if (units > (int64_t)UINT32_MAX || B * M > (int64_t)UINT32_MAX) return GTMS_ERR_INVALID_ARG;
     a.n_units = (uint32_t)units;
     a.n_planes = (uint32_t)(B * M);
-    a.k = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
+    // forward: scale * log2(e), so that exp is 2^x; backward: the scale itself
+    a.k = OP == OP_FWD ? (float)((double)scale * 1.4426950408889634074) : scale;
 
     hipStream_t hs = (hipStream_t)stream;
     hipError_t e;
     switch (dtype) {
-        case GTMS_F32: e = dispatch<DT_F32>(plan, a, hs); break;
-        case GTMS_F16: e = dispatch<DT_F16>(plan, a, hs); break;
-        default: e = dispatch<DT_BF16>(plan, a, hs); break;
+        case GTMS_F32: e = dispatch<OP, DT_F32>(plan, a, hs); break;
+        case GTMS_F16: e = dispatch<OP, DT_F16>(plan, a, hs); break;
+        default: e = dispatch<OP, DT_BF16>(plan, a, hs); break;
     }
     return e == hipSuccess ? GTMS_OK : GTMS_ERR_HIP;
 }
@@ -243,14 +270,28 @@ extern "C" {
 
 int gtms_forward(const void* in, void* out, const int32_t* seq_lens, int64_t B, int64_t M,
                  int64_t S, float scale, int dtype, void* stream) {
-    return gtms::forward_impl(in, out, seq_lens, B, M, S, scale, dtype, GTMS_PATH_AUTO, 0u,
-                              stream);
+    return gtms::run_impl<gtms::OP_FWD>(in, nullptr, out, seq_lens, B, M, S, scale, dtype,
+                                        GTMS_PATH_AUTO, 0u, stream);
 }
 
 int gtms_forward_ex(const void* in, void* out, const int32_t* seq_lens, int64_t B,
                     int64_t M, int64_t S, float scale, int dtype, int path, unsigned flags,
                     void* stream) {
-    return gtms::forward_impl(in, out, seq_lens, B, M, S, scale, dtype, path, flags, stream);
+    return gtms::run_impl<gtms::OP_FWD>(in, nullptr, out, seq_lens, B, M, S, scale, dtype, path,
+                                        flags, stream);
+}
+
+int gtms_backward(const void* y, const void* dy, void* dx, const int32_t* seq_lens, int64_t B,
+                  int64_t M, int64_t S, float scale, int dtype, void* stream) {
+    return gtms::run_impl<gtms::OP_BWD>(y, dy, dx, seq_lens, B, M, S, scale, dtype,
+                                        GTMS_PATH_AUTO, 0u, stream);
+}
+
+int gtms_backward_ex(const void* y, const void* dy, void* dx, const int32_t* seq_lens,
+                     int64_t B, int64_t M, int64_t S, float scale, int dtype, int path,
+                     unsigned flags, void* stream) {
+    return gtms::run_impl<gtms::OP_BWD>(y, dy, dx, seq_lens, B, M, S, scale, dtype, path, flags,
+                                        stream);
 }
 
 const char* gtms_status_string(int status) {
