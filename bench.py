@@ -165,20 +165,31 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
+    # the timed region: K back-to-back steps; two events on the launch stream bracket it,
+    # so the average launch duration is their interval over K (gaps between launches
+    # included, which makes it slightly pessimistic)
     stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.steps):
-        ev[i][0].record(stream)
         step(i)
-        ev[i][1].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kernel_ms = [a.elapsed_time(b) for a, b in ev]
-    avg_kernel_ms = float(np.mean(kernel_ms))
+    avg_kernel_ms = ev0.elapsed_time(ev1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
+
+    # after the timed region: per-launch events for the spread of single launch times
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(min(args.steps, 50))]
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        step(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    kernel_ms = [a.elapsed_time(b) for a, b in ev]
 
     if args.copy_calibration:  # plain copy of a known size, outside the timed region
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB

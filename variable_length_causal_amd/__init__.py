@@ -65,12 +65,18 @@ def version() -> int:
     return _load().gtms_version()
 
 
+_codes = None
+
+
 def _dtype_code(t) -> int:
-    import torch
-    codes = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
-    if t.dtype not in codes:
+    global _codes
+    if _codes is None:
+        import torch
+        _codes = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+    code = _codes.get(t.dtype)
+    if code is None:
         raise TypeError(f"unsupported dtype {t.dtype}; expected float32, float16 or bfloat16")
-    return codes[t.dtype]
+    return code
 
 
 def _check_scores(x, name="x"):
@@ -98,8 +104,27 @@ def _raise(st: int, what: str):
 
 
 def _stream_of(t):
+    """The current torch stream of t's device, as a hipStream_t."""
     import torch
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+class _on_device:
+    """Makes t's device current for the call (HIP launches go to the current device)."""
+
+    def __init__(self, t):
+        import torch
+        self.torch, self.idx, self.prev = torch, t.device.index, None
+
+    def __enter__(self):
+        cur = self.torch.cuda.current_device()
+        if cur != self.idx:
+            self.prev = cur
+            self.torch.cuda.set_device(self.idx)
+
+    def __exit__(self, *exc):
+        if self.prev is not None:
+            self.torch.cuda.set_device(self.prev)
 
 
 def forward(x, seq_lens, scale: float = 1.0, out=None, path: str = "auto", flags: int = 0):
@@ -118,7 +143,7 @@ def forward(x, seq_lens, scale: float = 1.0, out=None, path: str = "auto", flags
         raise ValueError("out must be a contiguous tensor of x's shape, dtype and device")
     B, M, S, _ = x.shape
     L = _load()
-    with torch.cuda.device(x.device):
+    with _on_device(x):
         if path == "auto" and flags == 0:
             st = L.gtms_forward(x.data_ptr(), out.data_ptr(), seq_lens.data_ptr(), B, M, S,
                                 float(scale), _dtype_code(x), _stream_of(x))
@@ -146,7 +171,7 @@ def backward(y, dy, seq_lens, scale: float = 1.0, out=None, path: str = "auto", 
         raise ValueError("out must be a contiguous tensor of y's shape, dtype and device")
     B, M, S, _ = y.shape
     L = _load()
-    with torch.cuda.device(y.device):
+    with _on_device(y):
         if path == "auto" and flags == 0:
             st = L.gtms_backward(y.data_ptr(), dy.data_ptr(), out.data_ptr(), seq_lens.data_ptr(),
                                  B, M, S, float(scale), _dtype_code(y), _stream_of(y))
