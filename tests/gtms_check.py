@@ -5,7 +5,7 @@ import numpy as np
 
 import workloads
 
-# spec tolerances: max |GPU - oracle fp64| on kept elements, per element type
+# tolerances: max |GPU - oracle fp64| on kept elements, per element type
 TOL = {workloads.F32: 2e-6, workloads.F16: 2e-3, workloads.BF16: 8e-3}
 
 
