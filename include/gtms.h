@@ -85,8 +85,11 @@ enum gtms_flags {
     GTMS_FLAG_PAIR_ROWS = 1u << 0,  /* one work unit = rows r and S-1-r (equal prefix work per
                                        unit; slower on MI355X, where adjacent rows written
                                        together keep HBM accesses local) */
-    GTMS_FLAG_XCD_ORDER = 1u << 1   /* give each XCD one contiguous range of rows (also
-                                       measured slower) */
+    GTMS_FLAG_PLAIN_ORDER = 1u << 1 /* hand work to the XCDs in the hardware's round-robin
+                                       block order. By default the blocks are renumbered so
+                                       that each XCD works through chunks of 16 consecutive
+                                       blocks, which keeps each XCD's accesses in one stretch
+                                       of memory; that measured 4-10% faster on MI355X */
 };
 
 /*

@@ -186,13 +186,13 @@ def test_very_long_rows_sampled():
 # ------------------------------------------------------------------------ properties
 
 def test_options_give_identical_bits():
-    """Row pairing and XCD block order change the schedule, not the arithmetic."""
+    """Row pairing and the block order change the schedule, not the arithmetic."""
     for dtype in DTYPES:
         for S, path in ((300, "wave"), (1000, "block"), (700, "stream")):
             lens = [S, 123, 0, 1]
             x = workloads.scores_cpu((4, 2, S, S), dtype, 1.0, seed=8000 + S)
             base = bits(workloads.to_storage(run_gpu(x, lens, 0.9, path).cpu()))
-            for flags in (g.FLAG_PAIR_ROWS, g.FLAG_XCD_ORDER, g.FLAG_PAIR_ROWS | g.FLAG_XCD_ORDER):
+            for flags in (g.FLAG_PAIR_ROWS, g.FLAG_PLAIN_ORDER, g.FLAG_PAIR_ROWS | g.FLAG_PLAIN_ORDER):
                 other = bits(workloads.to_storage(run_gpu(x, lens, 0.9, path, flags).cpu()))
                 assert np.array_equal(base, other), (DNAME[dtype], S, path, flags)
 

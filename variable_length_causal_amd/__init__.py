@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(HERE, "libgtms.so")
 # element-type, path and flag codes of include/gtms.h
 F32, F16, BF16 = 0, 1, 2
 PATH_AUTO, PATH_WAVE, PATH_BLOCK, PATH_STREAM = 0, 1, 2, 3
-FLAG_PAIR_ROWS, FLAG_XCD_ORDER = 1, 2
+FLAG_PAIR_ROWS, FLAG_PLAIN_ORDER = 1, 2
 PATHS = {"auto": PATH_AUTO, "wave": PATH_WAVE, "block": PATH_BLOCK, "stream": PATH_STREAM}
 
 _lib = None

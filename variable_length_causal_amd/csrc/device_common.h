@@ -180,13 +180,16 @@ template <class Op> __device__ __forceinline__ float wave_reduce(float v) {
 }
 
 // ------------------------------------------------------------------ block ordering
-// Blocks are dealt to the XCDs round-robin (block i runs on XCD i % 8). Renumber them so
-// that each XCD works through one contiguous range of logical blocks: neighbouring rows,
-// which can share a cache line at a row boundary, then meet in the same L2.
-__device__ __forceinline__ uint32_t xcd_order(uint32_t bid, uint32_t nblk) {
-    const uint32_t q = nblk / kXcds, rem = nblk % kXcds;
-    const uint32_t xcd = bid % kXcds, idx = bid / kXcds;
-    return xcd * q + (xcd < rem ? xcd : rem) + idx;
+// Blocks are dealt to the XCDs round-robin (block i runs on XCD i % 8), and each XCD then
+// advances through its share at its own pace. Renumber them so that each XCD works through
+// chunks of 2^shift consecutive logical blocks (XCD x takes chunks x, x + 8, x + 16, ...):
+// the blocks one XCD has in flight then cover one contiguous stretch of memory however far
+// the XCDs drift apart. Blocks past the last whole round of 8 chunks keep their number.
+__device__ __forceinline__ uint32_t xcd_chunked(uint32_t bid, uint32_t nblk, uint32_t shift) {
+    const uint32_t full = (nblk >> (shift + 3)) << (shift + 3);
+    if (bid >= full) return bid;
+    const uint32_t x = bid % kXcds, i = bid / kXcds;
+    return ((((i >> shift) * kXcds) + x) << shift) + (i & ((1u << shift) - 1u));
 }
 
 __device__ __forceinline__ int clamp_len(int32_t raw, int S) {

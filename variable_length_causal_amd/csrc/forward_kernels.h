@@ -55,6 +55,7 @@ struct FwdArgs {
     int row_bytes;             // S * element size
     float k;                   // forward: scale * log2(e); backward: scale
     unsigned flags;
+    uint32_t xcd_shift;        // F_XCD: log2 of the blocks in one XCD chunk
 };
 
 struct Unit {
@@ -268,7 +269,7 @@ __global__ __launch_bounds__(WPB * kWave) void fwd_wave(FwdArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t wave = WPB == 1 ? 0u : (uint32_t)uniform(threadIdx.x / kWave);
     const uint32_t nblk = gridDim.x;
-    const uint32_t blk = (a.flags & F_XCD) ? xcd_order(blockIdx.x, nblk) : blockIdx.x;
+    const uint32_t blk = (a.flags & F_XCD) ? xcd_chunked(blockIdx.x, nblk, a.xcd_shift) : blockIdx.x;
     for (uint64_t unit = (uint64_t)blk * WPB + wave; unit < a.n_units;
          unit += (uint64_t)nblk * WPB) {
         const Unit u = decode_unit((uint32_t)unit, a);
@@ -333,7 +334,7 @@ template <int DT, bool WIDE, int NV, int W, int SP>
 __global__ __launch_bounds__(W * kWave) void fwd_block(FwdArgs a) {
     __shared__ float part[2][2][W];  // [row of the unit][max, sum][wave]
     const uint32_t nblk = gridDim.x;
-    const uint32_t blk = (a.flags & F_XCD) ? xcd_order(blockIdx.x, nblk) : blockIdx.x;
+    const uint32_t blk = (a.flags & F_XCD) ? xcd_chunked(blockIdx.x, nblk, a.xcd_shift) : blockIdx.x;
     for (uint64_t unit = blk; unit < a.n_units; unit += nblk) {
         const Unit u = decode_unit((uint32_t)unit, a);
         const int L = clamp_len(a.seq_lens[u.plane / a.M], a.S);
@@ -408,7 +409,7 @@ template <int DT, bool WIDE, int W, int SP>
 __global__ __launch_bounds__(W * kWave) void fwd_stream(FwdArgs a) {
     __shared__ float part[2][2][W];
     const uint32_t nblk = gridDim.x;
-    const uint32_t blk = (a.flags & F_XCD) ? xcd_order(blockIdx.x, nblk) : blockIdx.x;
+    const uint32_t blk = (a.flags & F_XCD) ? xcd_chunked(blockIdx.x, nblk, a.xcd_shift) : blockIdx.x;
     for (uint64_t unit = blk; unit < a.n_units; unit += nblk) {
         const Unit u = decode_unit((uint32_t)unit, a);
         const int L = clamp_len(a.seq_lens[u.plane / a.M], a.S);

@@ -17,6 +17,11 @@ constexpr int kWaveWPB = 4;     // wavefronts per workgroup on the wave path
 constexpr int kMaxW = 16;       // wavefronts per workgroup on the block path, at most
 constexpr int kStreamW = 8;     // wavefronts per workgroup on the stream path
 constexpr int64_t kMaxGrid = int64_t(1) << 22;
+// Each XCD takes chunks of 2^4 consecutive blocks (unless GTMS_FLAG_PLAIN_ORDER). Measured on
+// MI355X over chunk sizes of 1 to 4096 blocks: 16 was fastest on every workload and path
+// (binary32 rows of 1000 elements four to a block, 16-bit rows of 4096 and 8192 elements one
+// to a block), 4-10% above the plain round-robin order.
+constexpr uint32_t kXcdChunkLog2 = 4;
 
 int esize_of(int dtype) { return dtype == GTMS_F32 ? 4 : 2; }
 
@@ -243,7 +248,8 @@ int run_impl(const void* x, const void* g, void* out, const int32_t* seq_lens, i
     a.row_bytes = (int)row_bytes;
     a.flags = 0;
     if (flags & GTMS_FLAG_PAIR_ROWS) a.flags |= F_PAIR;
-    if (flags & GTMS_FLAG_XCD_ORDER) a.flags |= F_XCD;
+    if (!(flags & GTMS_FLAG_PLAIN_ORDER)) a.flags |= F_XCD;
+    a.xcd_shift = kXcdChunkLog2;
     if (lines && plan.path != GTMS_PATH_STREAM) a.flags |= F_LINES;
     a.units_per_plane = (a.flags & F_PAIR) ? (uint32_t)((S + 1) / 2) : (uint32_t)S;
     const int64_t units = B * M * (int64_t)a.units_per_plane;
