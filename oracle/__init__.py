@@ -53,6 +53,21 @@ def _lens(seq_lens, n: int) -> np.ndarray:
     return sl
 
 
+def _nptr(a):
+    return None if a is None else _ptr(a)
+
+
+def mask_layout(mask: np.ndarray, B: int, M: int, S: int):
+    """A contiguous uint8 copy of a [B|1, M|1, S|1, S] mask and its byte strides for b, m and
+    r (zero where the dimension broadcasts)."""
+    mk = np.ascontiguousarray(np.asarray(mask).astype(np.uint8))
+    if mk.ndim != 4 or mk.shape[3] != S or any(d not in (1, n) for d, n in
+                                               zip(mk.shape[:3], (B, M, S))):
+        raise ValueError(f"mask shape {mk.shape} does not broadcast to [{B}, {M}, {S}, {S}]")
+    st = [mk.strides[i] if mk.shape[i] > 1 else 0 for i in range(3)]
+    return mk, st[0], st[1], st[2]
+
+
 class Oracle:
     """One loaded copy of the C oracle (the default one, or a test build of it)."""
 
@@ -67,6 +82,17 @@ class Oracle:
         lib.gtms_oracle_rows_f64.restype = i32
         lib.gtms_oracle_backward_f64.argtypes = [p, p, p, p, i64, i64, i64, f32, i32]
         lib.gtms_oracle_backward_f64.restype = i32
+        lib.gtms_oracle_band_f64.argtypes = [p, p, p, i64, i64, i64, i64, i64, f32, i32]
+        lib.gtms_oracle_band_f64.restype = i32
+        lib.gtms_oracle_band_backward_f64.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, f32,
+                                                      i32]
+        lib.gtms_oracle_band_backward_f64.restype = i32
+        lib.gtms_oracle_masked_f64.argtypes = [p, p, p, i64, i64, i64, p, i64, i64, i64, f32,
+                                               i32]
+        lib.gtms_oracle_masked_f64.restype = i32
+        lib.gtms_oracle_masked_backward_f64.argtypes = [p, p, p, p, i64, i64, i64, p, i64, i64,
+                                                        i64, f32, i32]
+        lib.gtms_oracle_masked_backward_f64.restype = i32
         lib.gtms_oracle_decode.argtypes = [ctypes.c_uint32, i32]
         lib.gtms_oracle_decode.restype = ctypes.c_double
         lib.gtms_oracle_encode.argtypes = [ctypes.c_double, i32]
@@ -132,6 +158,66 @@ class Oracle:
                      "gtms_oracle_backward_f64")
         return dx
 
+    # ---- mask variants: seq_lens may be None (every valid length is S)
+
+    def softmax_band_f64(self, x: np.ndarray, seq_lens, lo: int, hi: int, scale: float = 1.0,
+                         dtype: int = F32) -> np.ndarray:
+        """fp64 results of the band variant: (r, c) kept when lo <= c - r <= hi (and r, c
+        below the valid length)."""
+        x = _check(x, dtype)
+        B, M, S, S2 = x.shape
+        assert S == S2
+        sl = None if seq_lens is None else _lens(seq_lens, B)
+        y = np.empty(x.shape, dtype=np.float64)
+        self._status(self.lib.gtms_oracle_band_f64(_ptr(x), _ptr(y), _nptr(sl), B, M, S,
+                                                   int(lo), int(hi), scale, dtype),
+                     "gtms_oracle_band_f64")
+        return y
+
+    def band_backward_f64(self, y: np.ndarray, dy: np.ndarray, seq_lens, lo: int, hi: int,
+                          scale: float = 1.0, dtype: int = F32) -> np.ndarray:
+        y = _check(y, dtype)
+        dy = _check(dy, dtype)
+        B, M, S, S2 = y.shape
+        assert S == S2 and dy.shape == y.shape
+        sl = None if seq_lens is None else _lens(seq_lens, B)
+        dx = np.empty(y.shape, dtype=np.float64)
+        self._status(self.lib.gtms_oracle_band_backward_f64(_ptr(y), _ptr(dy), _ptr(dx),
+                                                            _nptr(sl), B, M, S, int(lo),
+                                                            int(hi), scale, dtype),
+                     "gtms_oracle_band_backward_f64")
+        return dx
+
+    def softmax_masked_f64(self, x: np.ndarray, mask: np.ndarray, seq_lens,
+                           scale: float = 1.0, dtype: int = F32) -> np.ndarray:
+        """fp64 results of the explicit-mask variant: mask has shape [B|1, M|1, S|1, S]
+        (a size-1 dimension broadcasts); an element is kept where the mask is non-zero."""
+        x = _check(x, dtype)
+        B, M, S, S2 = x.shape
+        assert S == S2
+        mk, sb, sm, sr = mask_layout(mask, B, M, S)
+        sl = None if seq_lens is None else _lens(seq_lens, B)
+        y = np.empty(x.shape, dtype=np.float64)
+        self._status(self.lib.gtms_oracle_masked_f64(_ptr(x), _ptr(y), _ptr(mk), sb, sm, sr,
+                                                     _nptr(sl), B, M, S, scale, dtype),
+                     "gtms_oracle_masked_f64")
+        return y
+
+    def masked_backward_f64(self, y: np.ndarray, dy: np.ndarray, mask: np.ndarray, seq_lens,
+                            scale: float = 1.0, dtype: int = F32) -> np.ndarray:
+        y = _check(y, dtype)
+        dy = _check(dy, dtype)
+        B, M, S, S2 = y.shape
+        assert S == S2 and dy.shape == y.shape
+        mk, sb, sm, sr = mask_layout(mask, B, M, S)
+        sl = None if seq_lens is None else _lens(seq_lens, B)
+        dx = np.empty(y.shape, dtype=np.float64)
+        self._status(self.lib.gtms_oracle_masked_backward_f64(_ptr(y), _ptr(dy), _ptr(dx),
+                                                              _ptr(mk), sb, sm, sr, _nptr(sl),
+                                                              B, M, S, scale, dtype),
+                     "gtms_oracle_masked_backward_f64")
+        return dx
+
     def decode(self, bits: int, dtype: int) -> float:
         return self.lib.gtms_oracle_decode(int(bits), dtype)
 
@@ -182,3 +268,19 @@ def decode(bits: int, dtype: int) -> float:
 
 def encode(v: float, dtype: int) -> int:
     return default().encode(v, dtype)
+
+
+def softmax_band_f64(*a, **k):
+    return default().softmax_band_f64(*a, **k)
+
+
+def band_backward_f64(*a, **k):
+    return default().band_backward_f64(*a, **k)
+
+
+def softmax_masked_f64(*a, **k):
+    return default().softmax_masked_f64(*a, **k)
+
+
+def masked_backward_f64(*a, **k):
+    return default().masked_backward_f64(*a, **k)

@@ -297,3 +297,156 @@ int gtms_oracle_backward_f64(const void* y, const void* dy, double* dx,
     }
     return OK;
 }
+
+/* ------------------------------------------------------------------------------------
+ * Mask variants. The page "优化ScaledMaskSoftmax算子" (ScaledMaskSoftmax article) applies a
+ * softmax under a general mask: masked scores are set to minus infinity before the
+ * exponentials (section 2.1), and a row whose every element is masked gives zeros
+ * (section 4.1, the guard for an all-zero mask row). Section 6 builds such masks for a
+ * local window (a lower-triangular band made with tril), for per-task masks broadcast
+ * over the batch, and for per-sample valid lengths. Here the kept set of a row is given as
+ * one flag per column, and the row's softmax runs over the flagged columns only.
+ * ------------------------------------------------------------------------------------ */
+
+/* Softmax of z_c = scale * x_c over the columns c with keep[c] != 0; other columns and rows
+ * with no kept column give 0. */
+static void softmax_kept_row(const void* x, const unsigned char* keep, int64_t S,
+                             double scale, int dtype, double* y) {
+    double mu = -INFINITY;
+    int64_t nkept = 0;
+    for (int64_t c = 0; c < S; ++c) {
+        if (!keep[c]) continue;
+        double z = scale * load_elem(x, c, dtype);
+        if (z > mu) mu = z;
+        ++nkept;
+    }
+    if (nkept == 0) {
+        for (int64_t c = 0; c < S; ++c) y[c] = 0.0;
+        return;
+    }
+    double den = 0.0;
+    for (int64_t c = 0; c < S; ++c) {
+        if (keep[c]) den += exp(scale * load_elem(x, c, dtype) - mu);
+    }
+    for (int64_t c = 0; c < S; ++c)
+        y[c] = keep[c] ? exp(scale * load_elem(x, c, dtype) - mu) / den : 0.0;
+}
+
+/* Gradient of the same row with respect to x, given its output y and upstream gradient g
+ * (the softmax derivative of the self-attention article, section 2.1, restricted to the
+ * kept columns): dx_c = scale * y_c * (g_c - sum_k g_k y_k) on kept columns, else 0. */
+static void backward_kept_row(const void* y, const void* g, const unsigned char* keep,
+                              int64_t S, double scale, int dtype, double* dx) {
+    double dot = 0.0;
+    for (int64_t c = 0; c < S; ++c) {
+        if (keep[c]) dot += load_elem(g, c, dtype) * load_elem(y, c, dtype);
+    }
+    for (int64_t c = 0; c < S; ++c)
+        dx[c] = keep[c] ? scale * load_elem(y, c, dtype) * (load_elem(g, c, dtype) - dot) : 0.0;
+}
+
+/* Band predicate: element (r, c) of a batch with valid length L is kept when r < L, c < L
+ * and lo <= c - r <= hi. lo <= -(S-1), hi = 0 is the grouped tril mask; hi = w alone is the
+ * article's tril(w) window; lo = -(w-1), hi = 0 is a causal window of w columns. */
+static int kept_band(int64_t r, int64_t c, int64_t L, int64_t lo, int64_t hi) {
+    if (r >= L || c >= L) return 0;
+    return c - r >= lo && c - r <= hi;
+}
+
+static int check_variant(const void* a, const void* b, int64_t B, int64_t M, int64_t S,
+                         int dtype, int64_t* n_elem) {
+    int ebits, pbits, bytes;
+    if (!format_of(dtype, &ebits, &pbits, &bytes)) return ERR_DTYPE;
+    if (B < 0 || M < 0 || S < 0) return ERR_ARG;
+    int64_t n = 1;
+    if (__builtin_mul_overflow(n, B, &n) || __builtin_mul_overflow(n, M, &n) ||
+        __builtin_mul_overflow(n, S, &n) || __builtin_mul_overflow(n, S, &n))
+        return ERR_ARG;
+    if (n > 0 && (!a || !b)) return ERR_ARG;
+    *n_elem = n;
+    return OK;
+}
+
+/* The kept flags of row r of plane (b, m), for the band (mask == NULL) or an explicit mask
+ * (element (b, m, r, c) at mask[b*sb + m*sm + r*sr + c], kept when non-zero). */
+static void row_flags(const unsigned char* mask, int64_t sb, int64_t sm, int64_t sr,
+                      int64_t lo, int64_t hi, int64_t b, int64_t m, int64_t r, int64_t L,
+                      int64_t S, unsigned char* keep) {
+    for (int64_t c = 0; c < S; ++c) {
+        if (mask)
+            keep[c] = r < L && c < L && mask[b * sb + m * sm + r * sr + c] != 0;
+        else
+            keep[c] = (unsigned char)kept_band(r, c, L, lo, hi);
+    }
+}
+
+/* Shared loop of the variant entry points. y_or_x is the forward input (forward) or the
+ * forward output (backward); g is the upstream gradient (backward) or NULL (forward). */
+static int run_variant(const void* y_or_x, const void* g, double* out,
+                       const unsigned char* mask, int64_t sb, int64_t sm, int64_t sr,
+                       int64_t lo, int64_t hi, const int32_t* seq_lens, int64_t B,
+                       int64_t M, int64_t S, float scale, int dtype) {
+    int ebits, pbits, bytes;
+    format_of(dtype, &ebits, &pbits, &bytes);
+    unsigned char* keep = (unsigned char*)malloc((size_t)S);
+    if (!keep) return ERR_ARG;
+    for (int64_t b = 0; b < B; ++b) {
+        int64_t L = seq_lens ? valid_length(seq_lens[b], S) : S;
+        for (int64_t m = 0; m < M; ++m) {
+            for (int64_t r = 0; r < S; ++r) {
+                int64_t off = ((b * M + m) * S + r) * S;
+                row_flags(mask, sb, sm, sr, lo, hi, b, m, r, L, S, keep);
+                const unsigned char* row = (const unsigned char*)y_or_x + off * bytes;
+                if (g)
+                    backward_kept_row(row, (const unsigned char*)g + off * bytes, keep, S,
+                                      (double)scale, dtype, out + off);
+                else
+                    softmax_kept_row(row, keep, S, (double)scale, dtype, out + off);
+            }
+        }
+    }
+    free(keep);
+    return OK;
+}
+
+int gtms_oracle_band_f64(const void* in, double* out, const int32_t* seq_lens, int64_t B,
+                         int64_t M, int64_t S, int64_t lo, int64_t hi, float scale,
+                         int dtype) {
+    int64_t n;
+    int st = check_variant(in, out, B, M, S, dtype, &n);
+    if (st != OK || n == 0) return st;
+    return run_variant(in, NULL, out, NULL, 0, 0, 0, lo, hi, seq_lens, B, M, S, scale, dtype);
+}
+
+int gtms_oracle_band_backward_f64(const void* y, const void* dy, double* dx,
+                                  const int32_t* seq_lens, int64_t B, int64_t M, int64_t S,
+                                  int64_t lo, int64_t hi, float scale, int dtype) {
+    int64_t n;
+    int st = check_variant(y, dx, B, M, S, dtype, &n);
+    if (st != OK || n == 0) return st;
+    if (!dy) return ERR_ARG;
+    return run_variant(y, dy, dx, NULL, 0, 0, 0, lo, hi, seq_lens, B, M, S, scale, dtype);
+}
+
+int gtms_oracle_masked_f64(const void* in, double* out, const uint8_t* mask, int64_t mask_sb,
+                           int64_t mask_sm, int64_t mask_sr, const int32_t* seq_lens,
+                           int64_t B, int64_t M, int64_t S, float scale, int dtype) {
+    int64_t n;
+    int st = check_variant(in, out, B, M, S, dtype, &n);
+    if (st != OK || n == 0) return st;
+    if (!mask || mask_sb < 0 || mask_sm < 0 || mask_sr < 0) return ERR_ARG;
+    return run_variant(in, NULL, out, mask, mask_sb, mask_sm, mask_sr, 0, 0, seq_lens, B, M,
+                       S, scale, dtype);
+}
+
+int gtms_oracle_masked_backward_f64(const void* y, const void* dy, double* dx,
+                                    const uint8_t* mask, int64_t mask_sb, int64_t mask_sm,
+                                    int64_t mask_sr, const int32_t* seq_lens, int64_t B,
+                                    int64_t M, int64_t S, float scale, int dtype) {
+    int64_t n;
+    int st = check_variant(y, dx, B, M, S, dtype, &n);
+    if (st != OK || n == 0) return st;
+    if (!dy || !mask || mask_sb < 0 || mask_sm < 0 || mask_sr < 0) return ERR_ARG;
+    return run_variant(y, dy, dx, mask, mask_sb, mask_sm, mask_sr, 0, 0, seq_lens, B, M, S,
+                       scale, dtype);
+}

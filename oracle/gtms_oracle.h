@@ -39,6 +39,27 @@ int gtms_oracle_backward_f64(const void* y, const void* dy, double* dx,
                              const int32_t* seq_lens, int64_t B, int64_t M, int64_t S,
                              float scale, int dtype);
 
+/* Mask variants (ScaledMaskSoftmax article, sections 2.1, 4.1 and 6). A row's softmax runs
+ * over its kept elements only; a row with no kept element is all zeros. seq_lens may be
+ * NULL, meaning every valid length is S; otherwise element (r, c) needs r < L_b and c < L_b.
+ *
+ * Band: element (r, c) is kept when lo <= c - r <= hi (besides the length condition).
+ * Masked: element (b, m, r, c) is kept when mask[b*mask_sb + m*mask_sm + r*mask_sr + c] is
+ * non-zero (strides in bytes, zero for a broadcast dimension; the column stride is 1). */
+int gtms_oracle_band_f64(const void* in, double* out, const int32_t* seq_lens, int64_t B,
+                         int64_t M, int64_t S, int64_t lo, int64_t hi, float scale,
+                         int dtype);
+int gtms_oracle_band_backward_f64(const void* y, const void* dy, double* dx,
+                                  const int32_t* seq_lens, int64_t B, int64_t M, int64_t S,
+                                  int64_t lo, int64_t hi, float scale, int dtype);
+int gtms_oracle_masked_f64(const void* in, double* out, const uint8_t* mask, int64_t mask_sb,
+                           int64_t mask_sm, int64_t mask_sr, const int32_t* seq_lens,
+                           int64_t B, int64_t M, int64_t S, float scale, int dtype);
+int gtms_oracle_masked_backward_f64(const void* y, const void* dy, double* dx,
+                                    const uint8_t* mask, int64_t mask_sb, int64_t mask_sm,
+                                    int64_t mask_sr, const int32_t* seq_lens, int64_t B,
+                                    int64_t M, int64_t S, float scale, int dtype);
+
 /* The element codec, exported so that it can be pinned on its own. */
 double gtms_oracle_decode(uint32_t bits, int dtype);
 uint32_t gtms_oracle_encode(double v, int dtype);

@@ -9,6 +9,9 @@ Sources of the facts:
     the masks and the output printed for its worked example (``golden/``), and the
     operator-behaviour listing (masked_fill with the most negative value, then softmax);
   * page "ops(8) self-attention CUDA (下)", section 2.1: the softmax derivative;
+  * page "优化ScaledMaskSoftmax算子", sections 2.1, 4.1 and 6: the mask variants (minus
+    infinity before the softmax, zero rows when every element is masked, masks built with
+    tril, broadcast per-task masks, per-sample length masks);
   * mathematics: closed forms of the softmax, shift invariance, finite differences;
   * libraries: numpy's binary16 and binary32 conversions, torch's softmax in float64,
     torch's exact bfloat16 widening.
@@ -448,8 +451,200 @@ def pin_backward(orc):
         assert abs(dx[b, m, r, j] - fd) <= 2e-5, (b, m, r, j, dx[b, m, r, j], fd)
 
 
+# ------------------------------------------------------------------------ mask variants
+# The ScaledMaskSoftmax article ("优化ScaledMaskSoftmax算子") masks scores with minus infinity
+# before the softmax (section 2.1), zeroes rows whose every element is masked (section
+# 4.1), and in section 6 builds masks with tril for a local window, broadcasts per-task
+# masks over the batch, and compares positions with per-sample lengths.
+
+def _torch_masked_softmax(z, keep):
+    """Reference in float64 with torch: masked_fill(-inf), softmax, rows without a kept
+    element set to zero."""
+    import torch
+    t = torch.as_tensor(z, dtype=torch.float64).masked_fill(~keep, float("-inf"))
+    y = t.softmax(-1)
+    return torch.where(keep.any(-1, keepdim=True), y, torch.zeros_like(y)).numpy()
+
+
+def _length_keep(S, L):
+    import torch
+    Lc = S if L is None else min(max(int(L), 0), S)
+    i = torch.arange(S)
+    return (i[:, None] < Lc) & (i[None, :] < Lc)
+
+
+def _band_keep(S, lo, hi, L):
+    """The band through torch's own triangle routines: tril(hi) keeps c - r <= hi and
+    triu(lo) keeps c - r >= lo (tril(w) is the article's window mask)."""
+    import torch
+    ones = torch.ones(S, S)
+    return (ones.tril(hi) * ones.triu(lo)).bool() & _length_keep(S, L)
+
+
+def pin_band_brute_force(orc):
+    """Band variant on tiny shapes, for many (lo, hi) and every length: matches torch's
+    masked softmax over the band built by tril/triu, and the naive exp(z)/sum exp(z) in
+    pure Python; masked elements are exactly +0."""
+    rng = np.random.default_rng(31)
+    for S in (1, 2, 3, 5, 8):
+        lens = list(range(-1, S + 2))
+        B = len(lens)
+        x = rng.uniform(-4.0, 4.0, size=(B, 1, S, S)).astype(np.float32)
+        scale = 0.7
+        sc = float(np.float32(scale))
+        for lo, hi in ((-S - 1, 0), (-2, 0), (0, 0), (-1, 1), (1, 3), (-S, S), (-3, -1),
+                       (-(10 ** 12), 2), (2, 1)):
+            y = orc.softmax_band_f64(x, lens, lo, hi, scale, F32)
+            for b, L in enumerate(lens):
+                keep = _band_keep(S, lo, hi, L)
+                ref = _torch_masked_softmax(x[b, 0].astype(np.float64) * sc, keep)
+                assert np.allclose(y[b, 0], ref, rtol=0, atol=1e-15), (S, lo, hi, L)
+                assert np.all(y[b, 0][~keep.numpy()] == 0.0)
+                assert not np.signbit(y[b, 0]).any()
+                for r in range(S):
+                    ks = [c for c in range(S) if keep[r, c]]
+                    if ks:
+                        den = sum(math.exp(sc * float(x[b, 0, r, c])) for c in ks)
+                        for c in ks:
+                            assert abs(y[b, 0, r, c] - math.exp(sc * float(x[b, 0, r, c])) / den) <= 1e-14
+        y = orc.softmax_band_f64(x, None, -1, 0, scale, F32)   # no lengths: every L is S
+        for b in range(B):
+            ref = _torch_masked_softmax(x[b, 0].astype(np.float64) * sc, _band_keep(S, -1, 0, None))
+            assert np.allclose(y[b, 0], ref, rtol=0, atol=1e-15)
+
+
+def pin_band_closed_forms(orc):
+    """(i) lo = hi = k: row r is one-hot at column r + k when that column is valid, else all
+    zeros. (ii) scale 0: each kept element is 1 / (number kept in its row). (iii) the
+    article's window tril(w) without lengths: row r keeps min(S, r + w + 1) columns.
+    (iv) lo <= -S, hi >= S with lengths (the article's per-sample length mask, for rows and
+    columns): each valid row is the plain softmax of its first L scores."""
+    rng = np.random.default_rng(32)
+    S = 9
+    lens = [9, 5, 1, 0, 12]
+    x = rng.normal(size=(5, 2, S, S)).astype(np.float32)
+    for k in (-3, -1, 0, 2, 8, 9):
+        y = orc.softmax_band_f64(x, lens, k, k, 1.3, F32)
+        for b, L in enumerate(lens):
+            Lc = min(L, S)
+            for r in range(S):
+                want = np.zeros(S)
+                if r < Lc and 0 <= r + k < Lc:
+                    want[r + k] = 1.0
+                assert np.array_equal(y[b, :, r], np.broadcast_to(want, (2, S))), (k, L, r)
+    for lo, hi in ((-2, 1), (-4, 0), (1, 5)):
+        y = orc.softmax_band_f64(x, lens, lo, hi, 0.0, F32)
+        for b, L in enumerate(lens):
+            Lc = min(L, S)
+            for r in range(S):
+                c0, c1 = max(0, r + lo), min(Lc - 1, r + hi)
+                n = c1 - c0 + 1 if r < Lc else 0
+                for c in range(S):
+                    want = 1.0 / n if n > 0 and c0 <= c <= c1 else 0.0
+                    assert abs(y[b, 0, r, c] - want) <= 1e-15, (lo, hi, L, r, c)
+    for w in (0, 1, 3):
+        y = orc.softmax_band_f64(x, None, -(10 ** 9), w, 0.0, F32)
+        for r in range(S):
+            n = min(S, r + w + 1)
+            assert np.allclose(y[:, :, r, :n], 1.0 / n, rtol=0, atol=1e-15)
+            assert np.all(y[:, :, r, n:] == 0.0)
+    # shift invariance far from zero: scores near 3000 at scale 0.5 (z near 1500, beyond
+    # where exp overflows) give the same rows as the unshifted scores
+    y0 = orc.softmax_band_f64(x, lens, -3, 1, 0.5, F32)
+    y1 = orc.softmax_band_f64((x.astype(np.float64) + 3000.0).astype(np.float32), lens, -3, 1,
+                              0.5, F32)
+    assert np.allclose(y0, y1, rtol=0, atol=2e-4)   # 3000 + x rounds x to 2^-12 in binary32
+    assert np.all((y0 == 0) == (y1 == 0))
+    from scipy.special import softmax as sp_softmax
+    y = orc.softmax_band_f64(x, lens, -S, S, 0.5, F32)
+    for b, L in enumerate(lens):
+        Lc = min(L, S)
+        if Lc:
+            ref = sp_softmax(0.5 * x[b, :, :Lc, :Lc].astype(np.float64), axis=-1)
+            assert np.allclose(y[b, :, :Lc, :Lc], ref, rtol=0, atol=1e-15)
+        assert np.all(y[b, :, Lc:] == 0.0) and np.all(y[b, :, :, Lc:] == 0.0)
+
+
+def pin_masked_brute_force(orc):
+    """Explicit-mask variant: random 0/1 masks of every broadcast layout (a shared [S, S]
+    mask, per-batch masks, per-head masks, per-sample key masks [B, 1, 1, S]), with and
+    without lengths, against torch's masked softmax on the expanded mask; a mask row of all
+    zeros gives a zero row; the value of a masked score never matters."""
+    import torch
+    rng = np.random.default_rng(33)
+    B, M, S = 3, 2, 7
+    x = rng.uniform(-4.0, 4.0, size=(B, M, S, S)).astype(np.float32)
+    for shape in ((1, 1, S, S), (B, 1, S, S), (1, M, S, S), (B, M, S, S), (B, 1, 1, S),
+                  (1, 1, 1, S)):
+        for density in (0.15, 0.5, 0.9):
+            mask = (rng.uniform(size=shape) < density).astype(np.uint8)
+            if shape[2] == S:
+                mask[..., 3, :] = 0       # an all-masked row
+            for lens in (None, [7, 4, 0]):
+                y = orc.softmax_masked_f64(x, mask, lens, 1.1, F32)
+                full = torch.as_tensor(np.broadcast_to(mask, (B, M, S, S)).copy()).bool()
+                for b in range(B):
+                    keep = full[b] & _length_keep(S, None if lens is None else lens[b])
+                    ref = _torch_masked_softmax(x[b].astype(np.float64) * float(np.float32(1.1)), keep)
+                    assert np.allclose(y[b], ref, rtol=0, atol=1e-15), (shape, density, lens, b)
+                    assert np.all(y[b][~keep.numpy()] == 0.0)
+                xp = x.copy()
+                xp[~np.broadcast_to(mask, x.shape).astype(bool)] = np.nan
+                yp = orc.softmax_masked_f64(xp, mask, lens, 1.1, F32)
+                assert np.array_equal(yp, y)
+
+
+def pin_variant_backward(orc):
+    """Backward of both variants equals torch's autograd gradient of its float64 masked
+    softmax (rows without a kept element contribute nothing)."""
+    import torch
+    rng = np.random.default_rng(34)
+    B, M, S = 2, 2, 6
+    x = rng.uniform(-2.0, 2.0, size=(B, M, S, S)).astype(np.float32)
+    g = rng.normal(size=(B, M, S, S)).astype(np.float32)
+    scale = 0.6
+    lens = [6, 3]
+    band = (-2, 1)
+    mask = (rng.uniform(size=(B, 1, S, S)) < 0.6).astype(np.uint8)
+    mask[0, 0, 2, :] = 0
+    cases = []
+    yb = orc.softmax_band_f64(x, lens, *band, scale, F32).astype(np.float32)
+    cases.append((orc.band_backward_f64(yb, g, lens, *band, scale, F32), yb,
+                  lambda b: _band_keep(S, band[0], band[1], lens[b]).expand(M, S, S)))
+    ym = orc.softmax_masked_f64(x, mask, lens, scale, F32).astype(np.float32)
+    cases.append((orc.masked_backward_f64(ym, g, mask, lens, scale, F32), ym,
+                  lambda b: torch.as_tensor(mask[b]).bool().expand(M, S, S) & _length_keep(S, lens[b])))
+    for dx, y, keep_of in cases:
+        for b in range(B):
+            keep = keep_of(b)
+            # the gradient of sum(g * softmax(scale * x)) at the point whose softmax is y:
+            # rebuild that point as log(y) on kept elements (softmax(log y) = y / sum y)
+            yt = torch.as_tensor(y[b].astype(np.float64))
+            z = torch.where(keep, torch.log(torch.where(keep, yt, torch.ones_like(yt))),
+                            torch.zeros_like(yt)) / float(np.float32(scale))
+            z.requires_grad_(True)
+            s = (z * float(np.float32(scale))).masked_fill(~keep, float("-inf")).softmax(-1)
+            s = torch.where(keep.any(-1, keepdim=True), s, torch.zeros_like(s))
+            (gd,) = torch.autograd.grad((s * torch.as_tensor(g[b].astype(np.float64))).sum(), z)
+            gd = torch.where(keep, gd, torch.zeros_like(gd)).numpy()
+            # the oracle differentiates at the rounded y; the rebuilt point differs from it by
+            # the normalisation of y, a relative change of order 2^-24
+            assert np.allclose(dx[b], gd, rtol=0, atol=1e-6), float(np.abs(dx[b] - gd).max())
+            assert np.all(dx[b][~keep.numpy()] == 0.0)
+    # masked cells of y and dy are never read: poisoning them changes no bit
+    for (dx, y, keep_of), fn in zip(cases, (
+            lambda yy, gg: orc.band_backward_f64(yy, gg, lens, *band, scale, F32),
+            lambda yy, gg: orc.masked_backward_f64(yy, gg, mask, lens, scale, F32))):
+        full = np.stack([keep_of(b).numpy() for b in range(B)])
+        yp, gp = y.copy(), g.copy()
+        yp[~full] = np.nan
+        gp[~full] = np.inf
+        assert np.array_equal(fn(yp, gp), dx)
+
+
 ALL_PINS = [
     pin_printed_masks, pin_printed_output, pin_row0, pin_row_sums, pin_exact_zeros,
     pin_brute_force, pin_closed_forms, pin_shift_and_scale, pin_masked_poison,
     pin_length_edges, pin_codec, pin_rounded_outputs, pin_rows_api, pin_backward,
+    pin_band_brute_force, pin_band_closed_forms, pin_masked_brute_force, pin_variant_backward,
 ]

@@ -32,6 +32,24 @@ MUTATIONS = {
                                "dx[off + c] = load_elem(y, off + c, dtype) *"),
     "row_column_swapped": ("if (kept(r, c, L))\n            y[c]",
                            "if (kept(c, r, L))\n            y[c]"),
+    # mask variants
+    "band_upper_edge_strict": ("return c - r >= lo && c - r <= hi;",
+                               "return c - r >= lo && c - r < hi;"),
+    "band_lower_edge_ignored": ("return c - r >= lo && c - r <= hi;", "return c - r <= hi;"),
+    "band_column_length_ignored": ("if (r >= L || c >= L) return 0;", "if (r >= L) return 0;"),
+    "variant_lengths_ignored": ("int64_t L = seq_lens ? valid_length(seq_lens[b], S) : S;",
+                                "int64_t L = S;"),
+    "mask_inverted": ("mask[b * sb + m * sm + r * sr + c] != 0",
+                      "mask[b * sb + m * sm + r * sr + c] == 0"),
+    "mask_row_stride_dropped": ("mask[b * sb + m * sm + r * sr + c]", "mask[b * sb + m * sm + c]"),
+    "mask_batch_ignored": ("mask[b * sb + m * sm + r * sr + c]", "mask[m * sm + r * sr + c]"),
+    "empty_variant_row_uniform": ("    if (nkept == 0) {\n        for (int64_t c = 0; c < S; ++c) y[c] = 0.0;",
+                                  "    if (nkept == 0) {\n        for (int64_t c = 0; c < S; ++c) y[c] = 1.0 / (double)S;"),
+    "variant_scale_dropped_in_max": ("        double z = scale * load_elem(x, c, dtype);\n        if (z > mu) mu = z;\n        ++nkept;\n    }\n    if (nkept == 0) {\n        for",
+                                     "        double z = load_elem(x, c, dtype);\n        if (z > mu) mu = z;\n        ++nkept;\n    }\n    if (nkept == 0) {\n        for"),
+    "variant_backward_sign": ("(load_elem(g, c, dtype) - dot)", "(load_elem(g, c, dtype) + dot)"),
+    "variant_backward_dot_unmasked": ("if (keep[c]) dot += load_elem(g, c, dtype) * load_elem(y, c, dtype);",
+                                      "dot += load_elem(g, c, dtype) * load_elem(y, c, dtype);"),
 }
 
 
