@@ -40,8 +40,9 @@ enum gtms_dtype { GTMS_F32 = 0, GTMS_F16 = 1, GTMS_BF16 = 2 };
 /* Status codes returned by every entry point. */
 enum gtms_status {
     GTMS_OK = 0,
-    GTMS_ERR_INVALID_ARG = 1, /* negative size, null pointer, B*M*S*S overflows int64,
-                                 S above GTMS_MAX_S, or in/out partially overlapping */
+    GTMS_ERR_INVALID_ARG = 1, /* negative size or mask stride, null pointer, B*M*S*S
+                                 overflows int64, S above GTMS_MAX_S, or in/out partially
+                                 overlapping */
     GTMS_ERR_DTYPE = 2,       /* unknown element type code */
     GTMS_ERR_ALIGN = 3,       /* a pointer not aligned to its element size */
     GTMS_ERR_HIP = 4,         /* the HIP runtime refused the launch */
@@ -119,6 +120,75 @@ int gtms_backward(const void* y, const void* dy, void* dx, const int32_t* seq_le
 int gtms_backward_ex(const void* y, const void* dy, void* dx, const int32_t* seq_lens,
                      int64_t B, int64_t M, int64_t S, float scale, int dtype, int path,
                      unsigned flags, void* stream);
+
+/*
+ * Mask variants (page "优化ScaledMaskSoftmax算子", the ScaledMaskSoftmax article): masked
+ * scores count as minus infinity before the softmax (section 2.1), and a row with no kept
+ * element is written as +0.0 (section 4.1, the guard for an all-masked row). Section 6 of
+ * the article builds such masks for a local window (with tril), per task (one mask
+ * broadcast over the batch) and per sample (positions below each sample's length); the
+ * two variants below cover those cases.
+ *
+ * Common to both: seq_lens may be NULL, which means every valid length is S; otherwise an
+ * element (r, c) of batch b can only be kept when r < L_b and c < L_b. Layout, dtype,
+ * in-place rules, streams and errors are those of gtms_forward / gtms_backward. Each row's
+ * softmax runs over its kept elements; every other element is +0.0.
+ */
+
+/*
+ * Band: element (r, c) is kept when lo <= c - r <= hi. The mask is computed, never loaded.
+ *   lo <= -(S-1), hi = 0      the grouped tril mask of gtms_forward (same results)
+ *   lo <= -(S-1), hi = w      the article's window mask tril(w)
+ *   lo = -(w-1), hi = 0       a causal sliding window of w columns
+ *   lo > hi                   every row is +0.0
+ * Any int64 values are accepted (c - r always lies in [-(S-1), S-1]).
+ */
+int gtms_forward_band(const void* in, void* out, const int32_t* seq_lens, int64_t B,
+                      int64_t M, int64_t S, int64_t lo, int64_t hi, float scale, int dtype,
+                      void* stream);
+
+/* Band forward with an explicit kernel choice and options (as gtms_forward_ex). */
+int gtms_forward_band_ex(const void* in, void* out, const int32_t* seq_lens, int64_t B,
+                         int64_t M, int64_t S, int64_t lo, int64_t hi, float scale, int dtype,
+                         int path, unsigned flags, void* stream);
+
+/*
+ * Explicit mask: element (b, m, r, c) is kept when the byte
+ *   mask[b * mask_stride_b + m * mask_stride_m + r * mask_stride_r + c]
+ * is non-zero (the reading of the article's mask where 1 marks a position to attend, as
+ * its section-6 examples build them). Strides are in bytes and must be >= 0; a stride of
+ * 0 broadcasts that dimension, so one [S, S] mask (strides 0, 0, S), per-batch or
+ * per-head masks, and per-sample key masks [B, 1, 1, S] (strides S, 0, 0) all fit. The
+ * column stride is 1. The caller guarantees that the S bytes of every mask row addressed
+ * for a row r < L_b lie in device memory (kernels read whole vectors, so columns up to
+ * the next multiple of 16 / element size past L_b - 1 may be read); the library cannot
+ * check the mask's extent. The mask may alias nothing that the call writes. With 16-byte vectors the mask's base
+ * address and strides must be multiples of 16 / element size (4 for binary32, 8 for
+ * 16-bit types); otherwise the call takes the element-wise path, which is slower but
+ * accepts any layout.
+ */
+int gtms_forward_masked(const void* in, void* out, const uint8_t* mask, int64_t mask_stride_b,
+                        int64_t mask_stride_m, int64_t mask_stride_r, const int32_t* seq_lens,
+                        int64_t B, int64_t M, int64_t S, float scale, int dtype, void* stream);
+
+/* Explicit-mask forward with an explicit kernel choice and options. */
+int gtms_forward_masked_ex(const void* in, void* out, const uint8_t* mask,
+                           int64_t mask_stride_b, int64_t mask_stride_m, int64_t mask_stride_r,
+                           const int32_t* seq_lens, int64_t B, int64_t M, int64_t S,
+                           float scale, int dtype, int path, unsigned flags, void* stream);
+
+/*
+ * Backward of the two variants: dx[c] = scale * y[c] * (dy[c] - sum over kept k of
+ * dy[k] * y[k]) on kept elements, +0.0 elsewhere (the derivative used by gtms_backward,
+ * over the variant's kept set). Arguments as gtms_backward_ex plus the variant's mask.
+ */
+int gtms_backward_band(const void* y, const void* dy, void* dx, const int32_t* seq_lens,
+                       int64_t B, int64_t M, int64_t S, int64_t lo, int64_t hi, float scale,
+                       int dtype, int path, unsigned flags, void* stream);
+int gtms_backward_masked(const void* y, const void* dy, void* dx, const uint8_t* mask,
+                         int64_t mask_stride_b, int64_t mask_stride_m, int64_t mask_stride_r,
+                         const int32_t* seq_lens, int64_t B, int64_t M, int64_t S, float scale,
+                         int dtype, int path, unsigned flags, void* stream);
 
 /* A static, human-readable description of a status code. */
 const char* gtms_status_string(int status);

@@ -1,6 +1,8 @@
 """Helpers of the GPU parity tests: the kept set, comparisons against the oracle."""
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 import workloads
@@ -57,3 +59,22 @@ def check_against_oracle(out_storage: np.ndarray, ref64: np.ndarray, lens, dtype
                 assert e <= tol, f"b={b} m={m}: max error {e:.3g} > {tol:.3g}"
                 worst = max(worst, e)
     return worst
+
+
+def esize(dtype: int) -> int:
+    return 4 if dtype == workloads.F32 else 2
+
+
+def path_ok(path, S, dtype, aligned=True):
+    """Whether a register-held path can take rows of S elements: a lane holds up to 16
+    slots of 16 bytes (rows whose byte length is a multiple of 16, on an aligned tensor)
+    or of one element otherwise; the block path has up to 16 wavefronts. A row of 16-byte
+    slots of at least 128 bytes may also write up to (128 - gcd(bytes, 128)) / 16 slots of
+    its predecessor's last line (torch allocations are 128-byte aligned)."""
+    if path in ("auto", "stream"):
+        return True
+    row_bytes = S * esize(dtype)
+    wide = aligned and row_bytes % 16 == 0
+    vec = 16 // esize(dtype) if wide else 1
+    slack = (128 - math.gcd(row_bytes, 128)) // 16 if wide and row_bytes >= 128 else 0
+    return -(-S // vec) + slack <= 64 * 16 * (16 if path == "block" else 1)

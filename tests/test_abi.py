@@ -93,3 +93,37 @@ def test_backward_argument_checks(lib):
     assert bwd(g=G + 2) == 3                             # misaligned dy
     assert bwd(B=0, y=0, g=0, dx=0, sl=0) == 0
     assert lib.gtms_backward_ex(Y, G, DX, SL, 1, 1, 4100, 1.0, 0, 1, 0, None) == 5
+
+
+def test_variant_argument_checks(lib):
+    X, Y, SL, MK = FAKE, FAKE * 4, FAKE * 8, FAKE * 16
+
+    def band(x=X, y=Y, sl=SL, S=8, lo=-8, hi=0, dtype=0, path=0):
+        return lib.gtms_forward_band_ex(x, y, sl, 1, 1, S, lo, hi, 1.0, dtype, path, 0, None)
+
+    def masked(x=X, y=Y, mk=MK, sb=0, sm=0, sr=8, sl=SL, B=1, S=8, dtype=0, path=0):
+        return lib.gtms_forward_masked_ex(x, y, mk, sb, sm, sr, sl, B, 1, S, 1.0, dtype, path,
+                                          0, None)
+    assert band(dtype=4) == 2
+    assert band(x=0) == 1
+    assert band(x=X + 2) == 3
+    assert band(x=X, y=X + 64) == 1                      # partial overlap
+    # no lengths is valid for the variants: the call gets past the argument checks and is
+    # only stopped by the unknown path
+    assert band(sl=0, path=9) == 5
+    assert masked(sl=0, path=9) == 5
+    assert band(lo=5, hi=-5, path=9) == 5                # an empty band is a valid request
+    assert masked(mk=0) == 1                             # no mask
+    assert masked(sr=-8) == 1                            # negative stride
+    assert masked(sb=-1, B=0, x=0, y=0, mk=0) == 1
+    assert masked(B=0, x=0, y=0, mk=0, sl=0) == 0        # empty: no-op
+    assert masked(dtype=2, x=X + 1) == 3
+    assert lib.gtms_forward_band(0, 0, 0, 0, 4, 4, 0, 0, 1.0, 0, None) == 0
+    assert lib.gtms_forward_masked(0, 0, 0, 0, 0, 4, 0, 0, 4, 4, 1.0, 0, None) == 0
+    G, DX = FAKE * 32, FAKE * 64
+    assert lib.gtms_backward_band(X, G, X, SL, 1, 1, 8, -8, 0, 1.0, 0, 0, 0, None) == 1
+    assert lib.gtms_backward_band(X, 0, DX, SL, 1, 1, 8, -8, 0, 1.0, 0, 0, 0, None) == 1
+    assert lib.gtms_backward_band(X, G, DX, 0, 1, 1, 8, -8, 0, 1.0, 0, 9, 0, None) == 5
+    assert lib.gtms_backward_masked(X, G, DX, 0, 0, 0, 8, SL, 1, 1, 8, 1.0, 0, 0, 0, None) == 1
+    assert lib.gtms_backward_masked(X, G, DX, MK, 0, -1, 8, SL, 1, 1, 8, 1.0, 0, 0, 0, None) == 1
+    assert lib.gtms_backward_masked(X, G, DX, MK, 0, 0, 8, 0, 1, 1, 8, 1.0, 0, 9, 0, None) == 5

@@ -12,14 +12,12 @@ element type, the rounding floor near zero.
 """
 from __future__ import annotations
 
-import math
-
 import numpy as np
 import pytest
 
 import oracle
 import workloads
-from gtms_check import bits, kept_mask, kept_row, to_f64
+from gtms_check import bits, kept_mask, kept_row, path_ok, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -34,18 +32,6 @@ DNAME = {workloads.F32: "f32", workloads.F16: "f16", workloads.BF16: "bf16"}
 U = {workloads.F32: 2.0 ** -21, workloads.F16: 2.0 ** -10, workloads.BF16: 2.0 ** -7}
 # half the spacing of the element type's subnormals: the rounding error floor near zero
 TINY = {workloads.F32: 2.0 ** -150, workloads.F16: 2.0 ** -25, workloads.BF16: 2.0 ** -134}
-
-
-def path_ok(path, S, dtype):
-    """As in test_gpu_parity: whether a register-held path can hold rows of S elements."""
-    if path in ("auto", "stream"):
-        return True
-    es = 4 if dtype == workloads.F32 else 2
-    row_bytes = S * es
-    wide = row_bytes % 16 == 0
-    vec = 16 // es if wide else 1
-    slack = (128 - math.gcd(row_bytes, 128)) // 16 if wide and row_bytes >= 128 else 0
-    return -(-S // vec) + slack <= 64 * 16 * (16 if path == "block" else 1)
 
 
 def check_rows(dx_st, ref, y_st, dy_st, lens_of_rows, rows_r, scale, dtype):

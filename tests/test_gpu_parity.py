@@ -8,14 +8,12 @@ every row (exact zeros, row sums).
 """
 from __future__ import annotations
 
-import math
-
 import numpy as np
 import pytest
 
 import oracle
 import workloads
-from gtms_check import TOL, bits, check_against_oracle, kept_mask, kept_row, to_f64
+from gtms_check import TOL, bits, check_against_oracle, kept_mask, kept_row, path_ok, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -27,25 +25,6 @@ import variable_length_causal_amd as g  # noqa: E402
 
 DTYPES = [workloads.F32, workloads.F16, workloads.BF16]
 DNAME = {workloads.F32: "f32", workloads.F16: "f16", workloads.BF16: "bf16"}
-
-
-def esize(dtype):
-    return 4 if dtype == workloads.F32 else 2
-
-
-def path_ok(path, S, dtype, aligned=True):
-    """Whether a register-held path can take rows of S elements: a lane holds up to 16
-    slots of 16 bytes (rows whose byte length is a multiple of 16, on an aligned tensor)
-    or of one element otherwise; the block path has up to 16 wavefronts. A row of 16-byte
-    slots of at least 128 bytes may also write up to (128 - gcd(bytes, 128)) / 16 slots of
-    its predecessor's last line (torch allocations are 128-byte aligned)."""
-    if path in ("auto", "stream"):
-        return True
-    row_bytes = S * esize(dtype)
-    wide = aligned and row_bytes % 16 == 0
-    vec = 16 // esize(dtype) if wide else 1
-    slack = (128 - math.gcd(row_bytes, 128)) // 16 if wide and row_bytes >= 128 else 0
-    return -(-S // vec) + slack <= 64 * 16 * (16 if path == "block" else 1)
 
 
 def run_gpu(x_cpu, lens, scale, path="auto", flags=0, out=None):

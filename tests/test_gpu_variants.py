@@ -1,0 +1,298 @@
+"""GPU parity of the mask variants (band and explicit mask) against the CPU oracle.
+
+The variants come from the ScaledMaskSoftmax article ("优化ScaledMaskSoftmax算子"): scores
+outside the kept set count as minus infinity (section 2.1), rows with no kept element are
+zeros (section 4.1), and section 6 builds window masks with tril, per-task masks
+broadcast over the batch, and per-sample length masks. Every test calls the library
+through its C ABI (the Python binding) and compares with the oracle's fp64 result:
+elements outside the kept set must be +0.0 bit for bit, kept elements within the element
+type's tolerance (binary32 2e-6, binary16 2e-3, bfloat16 8e-3). The kept set used for the
+bit check is built here from the definition, not taken from either side.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gtms_check import TOL, bits, path_ok, to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("GPU tests need a visible GPU", allow_module_level=True)
+
+import variable_length_causal_amd as g  # noqa: E402
+
+DTYPES = [workloads.F32, workloads.F16, workloads.BF16]
+DNAME = {workloads.F32: "f32", workloads.F16: "f16", workloads.BF16: "bf16"}
+PATHS = ("auto", "wave", "block", "stream")
+U = {workloads.F32: 2.0 ** -21, workloads.F16: 2.0 ** -10, workloads.BF16: 2.0 ** -7}
+TINY = {workloads.F32: 2.0 ** -150, workloads.F16: 2.0 ** -25, workloads.BF16: 2.0 ** -134}
+
+
+def length_keep(S, L):
+    Lc = S if L is None else min(max(int(L), 0), S)
+    i = np.arange(S)
+    return (i[:, None] < Lc) & (i[None, :] < Lc)
+
+
+def band_keep(S, L, lo, hi):
+    d = np.arange(S)[None, :] - np.arange(S)[:, None]
+    return (d >= lo) & (d <= hi) & length_keep(S, L)
+
+
+def expand_mask(mask, B, M, S):
+    return np.broadcast_to(np.asarray(mask).astype(bool), (B, M, S, S))
+
+
+def lens_dev(lens):
+    return None if lens is None else torch.as_tensor(np.asarray(lens, np.int32)).cuda()
+
+
+def check(out_dev, ref64, keep, dtype, tag):
+    """keep: bool [B, M, S, S]."""
+    st = workloads.to_storage(out_dev.cpu())
+    ob = bits(st)
+    assert not ob[~keep].any(), f"{tag}: nonzero bits outside the kept set"
+    if keep.any():
+        got = to_f64(st, dtype)
+        err = np.abs(got[keep] - ref64[keep])
+        assert np.all(np.isfinite(got[keep])), f"{tag}: non-finite kept output"
+        assert float(err.max()) <= TOL[dtype], f"{tag}: max error {float(err.max()):.3g}"
+
+
+def band_case(shape, dtype, lens, lo, hi, scale, paths, seed):
+    B, M, S, _ = shape
+    paths = [p for p in paths if path_ok(p, S, dtype)]
+    x = workloads.scores_cpu(shape, dtype, 1.0, seed)
+    ref = oracle.softmax_band_f64(workloads.to_storage(x), lens, lo, hi, scale, dtype)
+    keep = np.stack([np.broadcast_to(band_keep(S, None if lens is None else lens[b], lo, hi),
+                                     (M, S, S)) for b in range(B)])
+    xd = x.cuda()
+    for path in paths:
+        print(f"band shape={shape} {DNAME[dtype]} lens={lens} lo={lo} hi={hi} path={path}",
+              flush=True)
+        y = g.forward_band(xd, lens_dev(lens), lo, hi, scale, path=path)
+        torch.cuda.synchronize()
+        check(y, ref, keep, dtype, f"band {shape} {lens} [{lo},{hi}] {path}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DNAME[d])
+def test_band_sweep(dtype):
+    for S in (1, 5, 64, 65, 200, 1000, 1025):
+        bands = [(-S, 0), (-63, 0), (-1, 1), (0, 0), (-10 ** 12, 5), (3, 1), (-S, S),
+                 (2, 40), (-(S // 2), -(S // 4))]
+        for lens in ([S, max(1, S // 3), 0, S + 5], None):
+            for lo, hi in bands:
+                band_case((4, 1, S, S), dtype, lens, lo, hi, 0.8, PATHS, seed=S + lo % 97)
+
+
+def test_band_equals_tril_bits():
+    """lo <= -(S-1), hi = 0 is the grouped tril mask: the same bits as gtms_forward."""
+    for dtype, S in ((workloads.F32, 1000), (workloads.F16, 4096), (workloads.BF16, 520)):
+        lens = [S, S // 2, 7]
+        x = workloads.scores_cpu((3, 2, S, S), dtype, 1.0, 11).cuda()
+        sl = lens_dev(lens)
+        a = g.forward(x, sl, 0.5)
+        b = g.forward_band(x, sl, -S, 0, 0.5)
+        c = g.forward_band(x, sl, -(10 ** 15), 0, 0.5)
+        torch.cuda.synchronize()
+        sa = bits(workloads.to_storage(a.cpu()))
+        assert np.array_equal(sa, bits(workloads.to_storage(b.cpu())))
+        assert np.array_equal(sa, bits(workloads.to_storage(c.cpu())))
+
+
+def masked_case(shape, dtype, mask_np, lens, scale, paths, seed, as_bool=False, mask_dev=None):
+    B, M, S, _ = shape
+    paths = [p for p in paths if path_ok(p, S, dtype)]
+    x = workloads.scores_cpu(shape, dtype, 1.0, seed)
+    ref = oracle.softmax_masked_f64(workloads.to_storage(x), mask_np, lens, scale, dtype)
+    if mask_dev is None:
+        mask_dev = torch.as_tensor(mask_np.astype(bool) if as_bool else mask_np).cuda()
+    keep = expand_mask(mask_np, B, M, S) & np.stack(
+        [np.broadcast_to(length_keep(S, None if lens is None else lens[b]), (M, S, S))
+         for b in range(B)])
+    xd = x.cuda()
+    for path in paths:
+        print(f"masked shape={shape} {DNAME[dtype]} mask={tuple(mask_np.shape)} lens={lens} "
+              f"path={path}", flush=True)
+        y = g.forward_masked(xd, mask_dev, lens_dev(lens), scale, path=path)
+        torch.cuda.synchronize()
+        check(y, ref, keep, dtype, f"masked {shape} {tuple(mask_np.shape)} {lens} {path}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DNAME[d])
+def test_masked_layouts(dtype):
+    rng = np.random.default_rng(7)
+    B, M = 3, 2
+    for S in (7, 64, 300, 1000, 1030):
+        layouts = [(1, 1, S, S), (B, 1, S, S), (1, M, S, S), (B, M, S, S), (B, 1, 1, S)]
+        for li, shape in enumerate(layouts):
+            mask = (rng.uniform(size=shape) < 0.6).astype(np.uint8)
+            if shape[2] == S:
+                mask[..., S // 2, :] = 0   # an all-masked row
+            for lens in (None, [S, S // 3, 0]):
+                masked_case((B, M, S, S), dtype, mask, lens, 1.2, PATHS, seed=S + li,
+                            as_bool=(li % 2 == 1))
+
+
+def test_masked_unaligned_mask_rows():
+    """Mask rows at odd byte strides (a view into a wider buffer): the element-wise path."""
+    for dtype, S in ((workloads.F32, 256), (workloads.BF16, 1000)):
+        rng = np.random.default_rng(3)
+        wide = (rng.uniform(size=(1, 1, S, S + 1)) < 0.5).astype(np.uint8)
+        view_np = np.ascontiguousarray(wide[..., :S])
+        mdev = torch.as_tensor(wide).cuda()[..., :S]
+        assert mdev.stride(2) == S + 1
+        masked_case((2, 2, S, S), dtype, view_np, [S, S - 9], 1.0, ("auto", "wave", "block"),
+                    seed=5, mask_dev=mdev)
+
+
+def test_masked_tril_matches_forward():
+    """A tril mask of ones with lengths is the grouped tril mask. The kernels see a wider
+    column interval ([0, L-1] instead of [0, r]), which changes which lane sums which
+    elements, so results agree to rounding (same zeros, values within the tolerance)."""
+    for dtype, S in ((workloads.F32, 1000), (workloads.F16, 4096)):
+        lens = [S, S // 3]
+        x = workloads.scores_cpu((2, 2, S, S), dtype, 1.0, 21).cuda()
+        sl = lens_dev(lens)
+        tril = torch.ones(S, S, dtype=torch.uint8, device="cuda").tril()[None, None]
+        a = workloads.to_storage(g.forward(x, sl, 0.3).cpu())
+        b = workloads.to_storage(g.forward_masked(x, tril, sl, 0.3).cpu())
+        assert np.array_equal(bits(a) == 0, bits(b) == 0)
+        assert float(np.max(np.abs(to_f64(a, dtype) - to_f64(b, dtype)))) <= TOL[dtype]
+
+
+def test_variants_ignore_masked_scores():
+    """NaN and infinity outside the kept set change no bit of either variant."""
+    S, lens = 300, [300, 100]
+    for dtype in DTYPES:
+        x = workloads.scores_cpu((2, 2, S, S), dtype, 1.0, 31)
+        keep_b = np.stack([np.broadcast_to(band_keep(S, L, -40, 3), (2, S, S)) for L in lens])
+        rng = np.random.default_rng(9)
+        mask = (rng.uniform(size=(2, 1, S, S)) < 0.5).astype(np.uint8)
+        keep_m = expand_mask(mask, 2, 2, S) & np.stack(
+            [np.broadcast_to(length_keep(S, L), (2, S, S)) for L in lens])
+        mdev = torch.as_tensor(mask).cuda()
+        sl = lens_dev(lens)
+        for keep, run in ((keep_b, lambda t: g.forward_band(t, sl, -40, 3, 1.0)),
+                          (keep_m, lambda t: g.forward_masked(t, mdev, sl, 1.0))):
+            clean = run(x.cuda())
+            xp = x.clone()
+            kt = torch.as_tensor(keep)
+            xp[~kt] = float("nan")
+            xp[(~kt) & (torch.arange(S)[None, None, None, :] % 2 == 0)] = float("inf")
+            dirty = run(xp.cuda())
+            torch.cuda.synchronize()
+            assert np.array_equal(bits(workloads.to_storage(clean.cpu())),
+                                  bits(workloads.to_storage(dirty.cpu())))
+
+
+def test_variant_long_rows():
+    for dtype, S, lens in ((workloads.F16, 4096, [4096, 1500]), (workloads.BF16, 8192, [8000])):
+        paths = ("auto", "block", "stream")
+        band_case((len(lens), 1, S, S), dtype, lens, -511, 0, 0.125, paths, seed=41)
+        band_case((len(lens), 1, S, S), dtype, None, -(10 ** 9), 300, 0.125, paths, seed=42)
+        rng = np.random.default_rng(43)
+        mask = (rng.uniform(size=(1, 1, S, S)) < 0.3).astype(np.uint8)
+        masked_case((len(lens), 1, S, S), dtype, mask, lens, 0.125, ("auto", "stream"), seed=44)
+
+
+def grad_check(dx_dev, ref, y_st, dy_st, keep, scale, dtype, tag):
+    st = workloads.to_storage(dx_dev.cpu())
+    assert not bits(st)[~keep].any(), f"{tag}: nonzero bits outside the kept set"
+    got, yv, gv = to_f64(st, dtype), to_f64(y_st, dtype), to_f64(dy_st, dtype)
+    gmax = np.max(np.where(keep, np.abs(gv), 0.0), axis=-1, keepdims=True)
+    bound = U[dtype] * np.abs(ref) + 1e-5 * abs(scale) * yv * gmax + TINY[dtype]
+    err = np.abs(got - ref)
+    assert np.all(err[keep] <= bound[keep]), f"{tag}: {float(np.max((err - bound)[keep]))}"
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DNAME[d])
+def test_variant_backward(dtype):
+    rng = np.random.default_rng(51)
+    for S in (5, 64, 300, 1000):
+        B, M = 3, 2
+        lens = [S, S // 3 + 1, 0]
+        x = workloads.to_storage(workloads.scores_cpu((B, M, S, S), dtype, 1.0, S))
+        dy = workloads.to_storage(workloads.scores_cpu((B, M, S, S), dtype, 1.0, S + 1))
+        lo, hi = -(S // 4) - 1, 2
+        mask = (rng.uniform(size=(B, 1, S, S)) < 0.5).astype(np.uint8)
+        yb = workloads.to_storage(torch.as_tensor(
+            oracle.softmax_band_f64(x, lens, lo, hi, 0.9, dtype)).to(workloads.torch_dtype(dtype)))
+        ym = workloads.to_storage(torch.as_tensor(
+            oracle.softmax_masked_f64(x, mask, lens, 0.9, dtype)).to(workloads.torch_dtype(dtype)))
+        refb = oracle.band_backward_f64(yb, dy, lens, lo, hi, 0.9, dtype)
+        refm = oracle.masked_backward_f64(ym, dy, mask, lens, 0.9, dtype)
+        keep_b = np.stack([np.broadcast_to(band_keep(S, L, lo, hi), (M, S, S)) for L in lens])
+        keep_m = expand_mask(mask, B, M, S) & np.stack(
+            [np.broadcast_to(length_keep(S, L), (M, S, S)) for L in lens])
+        sl = lens_dev(lens)
+        mdev = torch.as_tensor(mask).cuda()
+        dyd = workloads.from_storage(dy, dtype).cuda()
+        for path in PATHS:
+            if not path_ok(path, S, dtype):
+                continue
+            print(f"variant backward S={S} {DNAME[dtype]} path={path}", flush=True)
+            dxb = g.backward_band(workloads.from_storage(yb, dtype).cuda(), dyd, sl, lo, hi, 0.9,
+                                  path=path)
+            dxm = g.backward_masked(workloads.from_storage(ym, dtype).cuda(), dyd, mdev, sl, 0.9,
+                                    path=path)
+            torch.cuda.synchronize()
+            grad_check(dxb, refb, yb, dy, keep_b, 0.9, dtype, f"band bwd S={S} {path}")
+            grad_check(dxm, refm, ym, dy, keep_m, 0.9, dtype, f"masked bwd S={S} {path}")
+
+
+def sampled_rows(x_dev, y_dev, rows, ref_row, dtype):
+    """Compare sampled rows (b, m, r) of a full-size launch with the oracle on one-row
+    planes: ref_row(b, r, row_storage) returns the fp64 reference row and its kept flags."""
+    xs = workloads.to_storage(torch.stack([x_dev[b, m, r] for b, m, r in rows]).cpu())
+    ys = workloads.to_storage(torch.stack([y_dev[b, m, r] for b, m, r in rows]).cpu())
+    got, yb = to_f64(ys, dtype), bits(ys)
+    for i, (b, m, r) in enumerate(rows):
+        ref, keep = ref_row(b, r, xs[i])
+        assert not yb[i][~keep].any(), (b, m, r)
+        if keep.any():
+            assert float(np.max(np.abs(got[i][keep] - ref[keep]))) <= TOL[dtype], (b, m, r)
+
+
+def test_full_size_window_and_key_masks_sampled():
+    """Full workload shapes: a causal window of 512 columns on binary16 32 x 1 x 4096, and
+    per-sample key masks [B, 1, 1, S] (the article's length mask) on binary32 3 x 64 x 1000."""
+    rng = np.random.default_rng(61)
+    w = workloads.WORKLOADS["scaled_f16_32x1x4096"]
+    lens = workloads.seq_lens(w)
+    x = workloads.scores_device(w.shape, w.dtype, w.sigma, w.x_seed, "cuda")
+    y = g.forward_band(x, torch.as_tensor(lens).cuda(), -511, 0, w.scale)
+    torch.cuda.synchronize()
+    S = w.S
+
+    def ref_band(b, r, row):
+        plane = np.zeros((1, 1, S, S), dtype=row.dtype)
+        plane[0, 0, r] = row
+        ref = oracle.softmax_band_f64(plane, [lens[b]], -511, 0, w.scale, w.dtype)[0, 0, r]
+        return ref, band_keep(S, lens[b], -511, 0)[r]
+    rows = [(int(rng.integers(w.B)), 0, int(rng.integers(S))) for _ in range(60)]
+    sampled_rows(x, y, rows, ref_band, w.dtype)
+    del x, y
+
+    w = workloads.WORKLOADS["readme_f32_3x64x1000"]
+    S = w.S
+    key_lens = [700, 1000, 10]
+    key = (np.arange(S)[None, :] < np.asarray(key_lens)[:, None]).astype(np.uint8)
+    key = key.reshape(w.B, 1, 1, S)
+    x = workloads.scores_device(w.shape, w.dtype, w.sigma, w.x_seed, "cuda")
+    y = g.forward_masked(x, torch.as_tensor(key).cuda(), None, w.scale)
+    torch.cuda.synchronize()
+
+    def ref_key(b, r, row):
+        plane = np.zeros((1, 1, S, S), dtype=row.dtype)
+        plane[0, 0, r] = row
+        ref = oracle.softmax_masked_f64(plane, key[b:b + 1], None, w.scale, w.dtype)[0, 0, r]
+        return ref, key[b, 0, 0].astype(bool)
+    rows = [(int(rng.integers(w.B)), int(rng.integers(w.M)), int(rng.integers(S)))
+            for _ in range(200)]
+    sampled_rows(x, y, rows, ref_key, w.dtype)

@@ -6,6 +6,9 @@ on the caller's current torch stream. Torch provides device memory and streams.
 
     y = forward(x, seq_lens, scale)      # x: [B, M, S, S] f32/f16/bf16 on the GPU
     dx = backward(y, dy, seq_lens, scale)
+    y = forward_band(x, seq_lens, lo, hi, scale)   # kept: lo <= c - r <= hi
+    y = forward_masked(x, mask, seq_lens, scale)   # kept: mask != 0 ([B|1, M|1, S|1, S])
+    dx = backward_band(...), backward_masked(...)  # their gradients
 
 There is no fallback: if the library is missing or cannot load, every call raises.
 """
@@ -44,6 +47,20 @@ def _load():
     lib.gtms_backward.restype = i32
     lib.gtms_backward_ex.argtypes = [p, p, p, p, i64, i64, i64, f32, i32, i32, u32, p]
     lib.gtms_backward_ex.restype = i32
+    lib.gtms_forward_band.argtypes = [p, p, p, i64, i64, i64, i64, i64, f32, i32, p]
+    lib.gtms_forward_band.restype = i32
+    lib.gtms_forward_band_ex.argtypes = [p, p, p, i64, i64, i64, i64, i64, f32, i32, i32, u32, p]
+    lib.gtms_forward_band_ex.restype = i32
+    lib.gtms_forward_masked.argtypes = [p, p, p, i64, i64, i64, p, i64, i64, i64, f32, i32, p]
+    lib.gtms_forward_masked.restype = i32
+    lib.gtms_forward_masked_ex.argtypes = [p, p, p, i64, i64, i64, p, i64, i64, i64, f32, i32,
+                                           i32, u32, p]
+    lib.gtms_forward_masked_ex.restype = i32
+    lib.gtms_backward_band.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, f32, i32, i32, u32, p]
+    lib.gtms_backward_band.restype = i32
+    lib.gtms_backward_masked.argtypes = [p, p, p, p, i64, i64, i64, p, i64, i64, i64, f32, i32,
+                                         i32, u32, p]
+    lib.gtms_backward_masked.restype = i32
     lib.gtms_status_string.argtypes = [i32]
     lib.gtms_status_string.restype = ctypes.c_char_p
     lib.gtms_version.argtypes = []
@@ -180,4 +197,127 @@ def backward(y, dy, seq_lens, scale: float = 1.0, out=None, path: str = "auto", 
                                     seq_lens.data_ptr(), B, M, S, float(scale), _dtype_code(y),
                                     PATHS[path], int(flags), _stream_of(y))
     _raise(st, "gtms_backward")
+    return out
+
+
+# ------------------------------------------------------------------------- mask variants
+
+def _lens_ptr(seq_lens, x):
+    if seq_lens is None:
+        return None
+    _check_lens(seq_lens, x)
+    return seq_lens.data_ptr()
+
+
+def _out_like(out, x):
+    import torch
+    if out is None:
+        return torch.empty_like(x)
+    if out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous() \
+            or out.device != x.device:
+        raise ValueError("out must be a contiguous tensor of the input's shape, dtype and device")
+    return out
+
+
+def mask_strides(mask, x):
+    """Byte strides (b, m, r) of a uint8/bool mask that broadcasts to x's [B, M, S, S]:
+    each leading dimension is 1 (broadcast, stride 0) or x's size; columns contiguous."""
+    import torch
+    if not mask.is_cuda or mask.device != x.device:
+        raise ValueError("mask must be on x's device")
+    if mask.dtype not in (torch.uint8, torch.bool):
+        raise TypeError("mask must be uint8 or bool (non-zero = kept)")
+    if mask.dim() != 4 or mask.shape[3] != x.shape[3]:
+        raise ValueError(f"mask must have shape [B|1, M|1, S|1, S], got {tuple(mask.shape)}")
+    st = []
+    for d in range(3):
+        n = mask.shape[d]
+        if n not in (1, x.shape[d]):
+            raise ValueError(f"mask dimension {d} is {n}, expected 1 or {x.shape[d]}")
+        st.append(0 if n == 1 else mask.stride(d))
+    if mask.shape[3] > 1 and mask.stride(3) != 1:
+        raise ValueError("mask columns must be contiguous")
+    return st
+
+
+def forward_band(x, seq_lens, lo: int, hi: int, scale: float = 1.0, out=None,
+                 path: str = "auto", flags: int = 0):
+    """Softmax over the band lo <= c - r <= hi of each row (and r, c below the valid
+    length; seq_lens may be None: every length is S). Rows with nothing kept are zeros."""
+    _check_scores(x)
+    out = _out_like(out, x)
+    B, M, S, _ = x.shape
+    L = _load()
+    with _on_device(x):
+        if path == "auto" and flags == 0:
+            st = L.gtms_forward_band(x.data_ptr(), out.data_ptr(), _lens_ptr(seq_lens, x), B, M,
+                                     S, int(lo), int(hi), float(scale), _dtype_code(x),
+                                     _stream_of(x))
+        else:
+            st = L.gtms_forward_band_ex(x.data_ptr(), out.data_ptr(), _lens_ptr(seq_lens, x), B,
+                                        M, S, int(lo), int(hi), float(scale), _dtype_code(x),
+                                        PATHS[path], int(flags), _stream_of(x))
+    _raise(st, "gtms_forward_band")
+    return out
+
+
+def forward_masked(x, mask, seq_lens=None, scale: float = 1.0, out=None, path: str = "auto",
+                   flags: int = 0):
+    """Softmax over the elements where ``mask`` (uint8/bool, [B|1, M|1, S|1, S], size-1 or
+    stride-0 dimensions broadcast) is non-zero, and r, c below the valid length."""
+    _check_scores(x)
+    sb, sm, sr = mask_strides(mask, x)
+    out = _out_like(out, x)
+    B, M, S, _ = x.shape
+    L = _load()
+    with _on_device(x):
+        if path == "auto" and flags == 0:
+            st = L.gtms_forward_masked(x.data_ptr(), out.data_ptr(), mask.data_ptr(), sb, sm, sr,
+                                       _lens_ptr(seq_lens, x), B, M, S, float(scale),
+                                       _dtype_code(x), _stream_of(x))
+        else:
+            st = L.gtms_forward_masked_ex(x.data_ptr(), out.data_ptr(), mask.data_ptr(), sb, sm,
+                                          sr, _lens_ptr(seq_lens, x), B, M, S, float(scale),
+                                          _dtype_code(x), PATHS[path], int(flags),
+                                          _stream_of(x))
+    _raise(st, "gtms_forward_masked")
+    return out
+
+
+def _check_grad_pair(y, dy):
+    _check_scores(y, "y")
+    _check_scores(dy, "dy")
+    if dy.shape != y.shape or dy.dtype != y.dtype or dy.device != y.device:
+        raise ValueError("dy must match y in shape, dtype and device")
+
+
+def backward_band(y, dy, seq_lens, lo: int, hi: int, scale: float = 1.0, out=None,
+                  path: str = "auto", flags: int = 0):
+    """Gradient of forward_band with respect to its input (out may be dy, not y)."""
+    _check_grad_pair(y, dy)
+    out = _out_like(out, y)
+    B, M, S, _ = y.shape
+    L = _load()
+    with _on_device(y):
+        st = L.gtms_backward_band(y.data_ptr(), dy.data_ptr(), out.data_ptr(),
+                                  _lens_ptr(seq_lens, y), B, M, S, int(lo), int(hi),
+                                  float(scale), _dtype_code(y), PATHS[path], int(flags),
+                                  _stream_of(y))
+    _raise(st, "gtms_backward_band")
+    return out
+
+
+def backward_masked(y, dy, mask, seq_lens=None, scale: float = 1.0, out=None,
+                    path: str = "auto", flags: int = 0):
+    """Gradient of forward_masked with respect to its input (out may be dy, not y)."""
+    _check_grad_pair(y, dy)
+    sb, sm, sr = mask_strides(mask, y)
+    out = _out_like(out, y)
+    B, M, S, _ = y.shape
+    L = _load()
+    with _on_device(y):
+        st = L.gtms_backward_masked(y.data_ptr(), dy.data_ptr(), out.data_ptr(), mask.data_ptr(),
+                                    sb, sm, sr, _lens_ptr(seq_lens, y), B, M, S, float(scale),
+                                    _dtype_code(y), PATHS[path], int(flags), _stream_of(y))
+    _raise(st, "gtms_backward_masked")
     return out

@@ -1,99 +1,127 @@
 // Backward kernels of the grouped tril mask softmax (gfx950).
 //
-// For a kept row r of plane p (r < L), with forward output y and upstream gradient g, the
-// softmax derivative dy_i/dz_j = y_i (delta_ij - y_j) (page "ops(8) self-attention CUDA
-// (下)", section 2.1) and z = scale * x give
-//   dx_c = scale * y_c * (g_c - D),   D = sum_{k <= r} g_k * y_k,
-// for c <= r; every other element of dx is +0 (masked elements and padded rows do not
-// reach the output). Arithmetic is fp32; results are rounded to nearest-even into the
+// For a row r of plane p with forward output y and upstream gradient g, the softmax
+// derivative dy_i/dz_j = y_i (delta_ij - y_j) (page "ops(8) self-attention CUDA (下)",
+// section 2.1) and z = scale * x give
+//   dx_c = scale * y_c * (g_c - D),   D = sum over kept k of g_k * y_k,
+// for kept c; every other element of dx is +0 (masked elements and padded rows do not
+// reach the output). The kept set follows the mask kind MK of the forward kernels. Arithmetic is fp32; results are rounded to nearest-even into the
 // element type.
 //
-// Memory: reads the kept prefixes of y and g (two triangles), writes every row of dx in
-// full. The layout, buffer-resource range checks, non-temporal stores, live-slot
-// specialisation and line ownership are those of the forward kernels; the reduction is a
-// plain sum (wave DPP + readlane, then LDS across the waves of a workgroup).
+// Memory: reads the kept intervals of y and g (for the tril mask, two triangles), writes
+// every row of dx in full. The layout, buffer-resource range checks, non-temporal stores,
+// live-slot specialisation and line ownership are those of the forward kernels; the
+// reduction is a plain sum (wave DPP + readlane, then LDS across the waves of a workgroup).
 #pragma once
 
 #include "forward_kernels.h"
 
 namespace gtms {
 
-template <class IO, int NA, int STRIDE>
+template <class IO, int NA, int STRIDE, int MK>
 struct GradPart {
+    using MIO = MaskIo<IO::VEC>;
     typename IO::raw_t ry[NA], rg[NA];
+    typename MIO::raw_t mk[MK == MK_MASK ? NA : 1];
     float d;  // this thread's part of D
 
-    __device__ __forceinline__ static int kept_count(int t, int j, int hv, int r) {
+    __device__ __forceinline__ static int kept_count(int t, int j, int hv, const Cols& k) {
         const int v = t + j * STRIDE - hv;
-        return v < 0 ? 0 : r + 1 - v * IO::VEC;
+        return v < 0 ? 0 : k.c1 + 1 - v * IO::VEC;
+    }
+    __device__ __forceinline__ static int kept_from(int t, int j, int hv, const Cols& k) {
+        return MK == MK_TRIL ? 0 : k.c0 - (t + j * STRIDE - hv) * IO::VEC;
+    }
+    __device__ __forceinline__ bool kept(int j, int q, int ka, int kc) const {
+        bool r = q < kc && (MK == MK_TRIL || q >= ka);
+        if constexpr (MK == MK_MASK) r = r && MIO::kept(mk[j], q);
+        return r;
     }
 
-    __device__ __forceinline__ void load(rsrc_t iny, rsrc_t ing, int t, int hv) {
+    __device__ __forceinline__ void load(rsrc_t iny, rsrc_t ing, rsrc_t min, int t, int hv,
+                                         const Cols& k) {
+        const int v0 = MK == MK_TRIL ? 0 : k.c0 / IO::VEC;
 #pragma unroll
         for (int j = 0; j < NA; ++j) {
             const int v = t + j * STRIDE - hv;
-            const int off = v < 0 ? kOutOfRange : v * IO::BYTES;
+            const int off = v < v0 ? kOutOfRange : v * IO::BYTES;
             ry[j] = IO::template load<kPolicyDefault>(iny, off);
             rg[j] = IO::template load<kPolicyDefault>(ing, off);
+            if constexpr (MK == MK_MASK) mk[j] = MIO::load(min, v < v0 ? kOutOfRange : v * IO::VEC);
         }
     }
 
-    __device__ __forceinline__ void dot(int t, int hv, int r) {
+    __device__ __forceinline__ void dot(int t, int hv, const Cols& k) {
         constexpr int VEC = IO::VEC;
         d = 0.0f;
 #pragma unroll
         for (int j = 0; j < NA; ++j) {
-            const int kc = kept_count(t, j, hv, r);
+            const int kc = kept_count(t, j, hv, k), ka = kept_from(t, j, hv, k);
             float fy[VEC], fg[VEC];
             IO::unpack(ry[j], fy);
             IO::unpack(rg[j], fg);
 #pragma unroll
-            for (int q = 0; q < VEC; ++q) d += q < kc ? fy[q] * fg[q] : 0.0f;
+            for (int q = 0; q < VEC; ++q) d += kept(j, q, ka, kc) ? fy[q] * fg[q] : 0.0f;
         }
     }
 
     template <int SP>
-    __device__ __forceinline__ void write(rsrc_t out, int t, int hv, int r, float scale,
+    __device__ __forceinline__ void write(rsrc_t out, int t, int hv, const Cols& k, float scale,
                                           float D) const {
         constexpr int VEC = IO::VEC;
 #pragma unroll
         for (int j = 0; j < NA; ++j) {
-            const int kc = kept_count(t, j, hv, r);
+            const int kc = kept_count(t, j, hv, k), ka = kept_from(t, j, hv, k);
             float fy[VEC], fg[VEC], o[VEC];
             IO::unpack(ry[j], fy);
             IO::unpack(rg[j], fg);
 #pragma unroll
-            for (int q = 0; q < VEC; ++q) o[q] = q < kc ? scale * fy[q] * (fg[q] - D) : 0.0f;
+            for (int q = 0; q < VEC; ++q)
+                o[q] = kept(j, q, ka, kc) ? scale * fy[q] * (fg[q] - D) : 0.0f;
             IO::template store<SP>(out, (t + j * STRIDE) * IO::BYTES, IO::pack(o));
         }
     }
 };
 
+// Buffer resources over the row's interval [0, c1] of y, g and (explicit mask) the mask.
+struct GradRows {
+    rsrc_t y, g, m;
+};
+
+template <class IO, int MK>
+__device__ __forceinline__ GradRows grad_rows(const FwdArgs& a, uint32_t plane, int r, int nin) {
+    GradRows q;
+    q.y = make_rsrc(row_ptr(a.x, plane, r, a), (uint32_t)(nin * IO::BYTES));
+    q.g = make_rsrc(row_ptr(a.g, plane, r, a), (uint32_t)(nin * IO::BYTES));
+    q.m = MK == MK_MASK ? make_rsrc(mask_row(a, plane, r), (uint32_t)(nin * IO::VEC)) : q.y;
+    return q;
+}
+
 // ---------------------------------------------------------------------------- bwd_wave
-template <int DT, bool WIDE, int NV, int SP>
+template <int DT, bool WIDE, int NV, int SP, int MK>
 __device__ __forceinline__ void bwd_wave_row(const FwdArgs& a, uint32_t plane, int r, int L,
                                              int lane) {
     using IO = Io<DT, WIDE>;
-    const Span sp = row_span<IO::BYTES / IO::VEC>(a, plane, r, L);
+    const Span sp = row_span<MK, IO::BYTES / IO::VEC>(a, plane, r, L);
     const rsrc_t out = make_rsrc(sp.out, sp.out_bytes);
-    if (r >= L) {
+    const Cols k = kept_cols<MK>(a, r, L);
+    if (k.empty()) {
         write_zero_slots<IO, 0, NV, kWave, SP>(out, lane);
         return;
     }
-    const int nin = r / IO::VEC + 1;
-    const rsrc_t iny = make_rsrc(row_ptr(a.x, plane, r, a), (uint32_t)(nin * IO::BYTES));
-    const rsrc_t ing = make_rsrc(row_ptr(a.g, plane, r, a), (uint32_t)(nin * IO::BYTES));
+    const int nin = k.c1 / IO::VEC + 1;
+    const GradRows in = grad_rows<IO, MK>(a, plane, r, nin);
     const int hv = sp.hv;
     with_live_slots<NV>((nin + hv + kWave - 1) / kWave, [&]<int NA>() {
-        GradPart<IO, NA, kWave> p;
-        p.load(iny, ing, lane, hv);
+        GradPart<IO, NA, kWave, MK> p;
+        p.load(in.y, in.g, in.m, lane, hv, k);
         write_zero_slots<IO, NA, NV, kWave, SP>(out, lane);
-        p.dot(lane, hv, r);
-        p.template write<SP>(out, lane, hv, r, a.k, wave_reduce<OpSum>(p.d));
+        p.dot(lane, hv, k);
+        p.template write<SP>(out, lane, hv, k, a.k, wave_reduce<OpSum>(p.d));
     });
 }
 
-template <int DT, bool WIDE, int NV, int WPB, int SP>
+template <int DT, bool WIDE, int NV, int WPB, int SP, int MK>
 __global__ __launch_bounds__(WPB * kWave) void bwd_wave(FwdArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t wave = WPB == 1 ? 0u : (uint32_t)uniform(threadIdx.x / kWave);
@@ -102,86 +130,96 @@ __global__ __launch_bounds__(WPB * kWave) void bwd_wave(FwdArgs a) {
     for (uint64_t unit = (uint64_t)blk * WPB + wave; unit < a.n_units;
          unit += (uint64_t)nblk * WPB) {
         const Unit u = decode_unit((uint32_t)unit, a);
-        const int L = clamp_len(a.seq_lens[u.plane / a.M], a.S);
-        bwd_wave_row<DT, WIDE, NV, SP>(a, u.plane, u.r0, L, lane);
-        if (u.r1 >= 0) bwd_wave_row<DT, WIDE, NV, SP>(a, u.plane, u.r1, L, lane);
+        const int L = valid_len<MK>(a, u.plane);
+        bwd_wave_row<DT, WIDE, NV, SP, MK>(a, u.plane, u.r0, L, lane);
+        if (u.r1 >= 0) bwd_wave_row<DT, WIDE, NV, SP, MK>(a, u.plane, u.r1, L, lane);
     }
 }
 
 // --------------------------------------------------------------------------- bwd_block
-template <int DT, bool WIDE, int NV, int W, int SP>
+template <int DT, bool WIDE, int NV, int W, int SP, int MK>
 __device__ __forceinline__ void bwd_block_row(const FwdArgs& a, uint32_t plane, int r, int L,
                                               float* pd) {
     using IO = Io<DT, WIDE>;
     constexpr int T = W * kWave;
     const int t = threadIdx.x;
-    const Span sp = row_span<IO::BYTES / IO::VEC>(a, plane, r, L);
+    const Span sp = row_span<MK, IO::BYTES / IO::VEC>(a, plane, r, L);
     const rsrc_t out = make_rsrc(sp.out, sp.out_bytes);
-    if (r >= L) {
+    const Cols k = kept_cols<MK>(a, r, L);
+    if (k.empty()) {
         write_zero_slots<IO, 0, NV, T, SP>(out, t);
         return;
     }
     const int wave = uniform(t / kWave);
-    const int nin = r / IO::VEC + 1;
-    const rsrc_t iny = make_rsrc(row_ptr(a.x, plane, r, a), (uint32_t)(nin * IO::BYTES));
-    const rsrc_t ing = make_rsrc(row_ptr(a.g, plane, r, a), (uint32_t)(nin * IO::BYTES));
+    const int nin = k.c1 / IO::VEC + 1;
+    const GradRows in = grad_rows<IO, MK>(a, plane, r, nin);
     const int hv = sp.hv;
     with_live_slots<NV>((nin + hv + T - 1) / T, [&]<int NA>() {
-        GradPart<IO, NA, T> p;
-        p.load(iny, ing, t, hv);
+        GradPart<IO, NA, T, MK> p;
+        p.load(in.y, in.g, in.m, t, hv, k);
         write_zero_slots<IO, NA, NV, T, SP>(out, t);
-        p.dot(t, hv, r);
+        p.dot(t, hv, k);
         const float dw = wave_reduce<OpSum>(p.d);
         if ((t & (kWave - 1)) == 0) pd[wave] = dw;
         __syncthreads();
         float D = 0.0f;
 #pragma unroll
         for (int w = 0; w < W; ++w) D += pd[w];
-        p.template write<SP>(out, t, hv, r, a.k, D);
+        p.template write<SP>(out, t, hv, k, a.k, D);
     });
 }
 
-template <int DT, bool WIDE, int NV, int W, int SP>
+template <int DT, bool WIDE, int NV, int W, int SP, int MK>
 __global__ __launch_bounds__(W * kWave) void bwd_block(FwdArgs a) {
     __shared__ float part[2][W];  // [row of the unit][wave]
     const uint32_t nblk = gridDim.x;
     const uint32_t blk = (a.flags & F_XCD) ? xcd_chunked(blockIdx.x, nblk, a.xcd_shift) : blockIdx.x;
     for (uint64_t unit = blk; unit < a.n_units; unit += nblk) {
         const Unit u = decode_unit((uint32_t)unit, a);
-        const int L = clamp_len(a.seq_lens[u.plane / a.M], a.S);
-        bwd_block_row<DT, WIDE, NV, W, SP>(a, u.plane, u.r0, L, part[0]);
-        if (u.r1 >= 0) bwd_block_row<DT, WIDE, NV, W, SP>(a, u.plane, u.r1, L, part[1]);
+        const int L = valid_len<MK>(a, u.plane);
+        bwd_block_row<DT, WIDE, NV, W, SP, MK>(a, u.plane, u.r0, L, part[0]);
+        if (u.r1 >= 0) bwd_block_row<DT, WIDE, NV, W, SP, MK>(a, u.plane, u.r1, L, part[1]);
         __syncthreads();  // the next unit rewrites the partials
     }
 }
 
 // -------------------------------------------------------------------------- bwd_stream
-// Rows of any length: pass 1 accumulates D, pass 2 re-reads both prefixes and writes.
-template <int DT, bool WIDE, int W, int SP>
+// Rows of any length: pass 1 accumulates D, pass 2 re-reads both intervals and writes.
+template <int DT, bool WIDE, int W, int SP, int MK>
 __device__ __forceinline__ void bwd_stream_row(const FwdArgs& a, uint32_t plane, int r, int L,
                                                float* pd) {
     using IO = Io<DT, WIDE>;
+    using MIO = MaskIo<IO::VEC>;
     constexpr int VEC = IO::VEC;
     constexpr int T = W * kWave;
     const int t = threadIdx.x;
     const int nraw = a.row_bytes / IO::BYTES;
     const rsrc_t out = make_rsrc(row_ptr(a.y, plane, r, a), (uint32_t)a.row_bytes);
-    if (r >= L) {
+    const Cols k = kept_cols<MK>(a, r, L);
+    if (k.empty()) {
         for (int v = t; v < nraw; v += T) IO::template store<SP>(out, v * IO::BYTES, IO::zero());
         return;
     }
     const int wave = uniform(t / kWave);
-    const int nin = r / VEC + 1;
-    const rsrc_t iny = make_rsrc(row_ptr(a.x, plane, r, a), (uint32_t)(nin * IO::BYTES));
-    const rsrc_t ing = make_rsrc(row_ptr(a.g, plane, r, a), (uint32_t)(nin * IO::BYTES));
+    const int v0 = k.c0 / VEC, nin = k.c1 / VEC + 1;
+    const GradRows in = grad_rows<IO, MK>(a, plane, r, nin);
+    for (int v = t; v < v0; v += T) IO::template store<SP>(out, v * IO::BYTES, IO::zero());
     for (int v = nin + t; v < nraw; v += T) IO::template store<SP>(out, v * IO::BYTES, IO::zero());
+    auto kept = [&](int v, int e, const typename MIO::raw_t& mb) {
+        const int c = v * VEC + e;
+        bool r = c >= k.c0 && c <= k.c1;
+        if constexpr (MK == MK_MASK) r = r && MIO::kept(mb, e);
+        return r;
+    };
     float d = 0.0f;
-    for (int v = t; v < nin; v += T) {
+    for (int v = v0 + t; v < nin; v += T) {
         float fy[VEC], fg[VEC];
-        IO::unpack(IO::template load<kPolicyDefault>(iny, v * IO::BYTES), fy);
-        IO::unpack(IO::template load<kPolicyDefault>(ing, v * IO::BYTES), fg);
+        IO::unpack(IO::template load<kPolicyDefault>(in.y, v * IO::BYTES), fy);
+        IO::unpack(IO::template load<kPolicyDefault>(in.g, v * IO::BYTES), fg);
+        typename MIO::raw_t mb{};
+        if constexpr (MK == MK_MASK) mb = MIO::load(in.m, v * VEC);
 #pragma unroll
-        for (int q = 0; q < VEC; ++q) d += v * VEC + q <= r ? fy[q] * fg[q] : 0.0f;
+        for (int q = 0; q < VEC; ++q) d += kept(v, q, mb) ? fy[q] * fg[q] : 0.0f;
     }
     const float dw = wave_reduce<OpSum>(d);
     if ((t & (kWave - 1)) == 0) pd[wave] = dw;
@@ -189,26 +227,28 @@ __device__ __forceinline__ void bwd_stream_row(const FwdArgs& a, uint32_t plane,
     float D = 0.0f;
 #pragma unroll
     for (int w = 0; w < W; ++w) D += pd[w];
-    for (int v = t; v < nin; v += T) {
+    for (int v = v0 + t; v < nin; v += T) {
         float fy[VEC], fg[VEC], o[VEC];
-        IO::unpack(IO::template load<kPolicyDefault>(iny, v * IO::BYTES), fy);
-        IO::unpack(IO::template load<kPolicyDefault>(ing, v * IO::BYTES), fg);
+        IO::unpack(IO::template load<kPolicyDefault>(in.y, v * IO::BYTES), fy);
+        IO::unpack(IO::template load<kPolicyDefault>(in.g, v * IO::BYTES), fg);
+        typename MIO::raw_t mb{};
+        if constexpr (MK == MK_MASK) mb = MIO::load(in.m, v * VEC);
 #pragma unroll
-        for (int q = 0; q < VEC; ++q) o[q] = v * VEC + q <= r ? a.k * fy[q] * (fg[q] - D) : 0.0f;
+        for (int q = 0; q < VEC; ++q) o[q] = kept(v, q, mb) ? a.k * fy[q] * (fg[q] - D) : 0.0f;
         IO::template store<SP>(out, v * IO::BYTES, IO::pack(o));
     }
 }
 
-template <int DT, bool WIDE, int W, int SP>
+template <int DT, bool WIDE, int W, int SP, int MK>
 __global__ __launch_bounds__(W * kWave) void bwd_stream(FwdArgs a) {
     __shared__ float part[2][W];
     const uint32_t nblk = gridDim.x;
     const uint32_t blk = (a.flags & F_XCD) ? xcd_chunked(blockIdx.x, nblk, a.xcd_shift) : blockIdx.x;
     for (uint64_t unit = blk; unit < a.n_units; unit += nblk) {
         const Unit u = decode_unit((uint32_t)unit, a);
-        const int L = clamp_len(a.seq_lens[u.plane / a.M], a.S);
-        bwd_stream_row<DT, WIDE, W, SP>(a, u.plane, u.r0, L, part[0]);
-        if (u.r1 >= 0) bwd_stream_row<DT, WIDE, W, SP>(a, u.plane, u.r1, L, part[1]);
+        const int L = valid_len<MK>(a, u.plane);
+        bwd_stream_row<DT, WIDE, W, SP, MK>(a, u.plane, u.r0, L, part[0]);
+        if (u.r1 >= 0) bwd_stream_row<DT, WIDE, W, SP, MK>(a, u.plane, u.r1, L, part[1]);
         __syncthreads();
     }
 }

@@ -152,6 +152,36 @@ template <> struct Io<DT_BF16, true> : Io16Wide<DT_BF16> {};
 template <> struct Io<DT_F16, false> : Io16Narrow<DT_F16> {};
 template <> struct Io<DT_BF16, false> : Io16Narrow<DT_BF16> {};
 
+// ------------------------------------------------------------------ explicit mask bytes
+// The kept flags of one vector of VEC elements from a byte mask (non-zero = kept), loaded
+// as one VEC-byte access at a byte offset that is a multiple of VEC.
+template <int VEC> struct MaskIo;
+template <> struct MaskIo<1> {
+    using raw_t = uint32_t;
+    __device__ __forceinline__ static raw_t load(rsrc_t r, int off) {
+        return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, kPolicyDefault);
+    }
+    __device__ __forceinline__ static bool kept(raw_t m, int) { return m != 0; }
+};
+template <> struct MaskIo<4> {
+    using raw_t = uint32_t;
+    __device__ __forceinline__ static raw_t load(rsrc_t r, int off) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kPolicyDefault);
+    }
+    __device__ __forceinline__ static bool kept(raw_t m, int q) { return (m >> (8 * q)) & 0xFFu; }
+};
+template <> struct MaskIo<8> {
+    struct raw_t { uint32_t lo, hi; };
+    __device__ __forceinline__ static raw_t load(rsrc_t r, int off) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kPolicyDefault);
+        const uint32_t lo = v[0], hi = v[1];
+        return {lo, hi};
+    }
+    __device__ __forceinline__ static bool kept(raw_t m, int q) {
+        return ((q < 4 ? m.lo : m.hi) >> (8 * (q & 3))) & 0xFFu;
+    }
+};
+
 // ------------------------------------------------------------------ wave64 reductions
 template <int CTRL> __device__ __forceinline__ float dpp(float v) {
     // every lane named by the butterfly patterns below exists, so bound_ctrl is irrelevant

@@ -28,9 +28,21 @@
 //   fwd_stream one workgroup per row, two passes (online max/sum, then normalise) for rows
 //              too long for registers.
 // A work unit is one row, or optionally the pair (r, S-1-r), whose kept prefixes add up to
-// S+1 columns whatever r is. Workgroups are numbered in row order by default: the rows
-// written at any moment then sit close together in memory, which HBM rewards (measured on
-// MI355X: pairing rows, or giving each XCD its own row range, cost 5-30%).
+// S+1 columns whatever r is. Units are taken in row order, each XCD working through chunks
+// of consecutive workgroups (xcd_chunked): the rows written at any moment then sit close
+// together in memory, which HBM rewards (measured on MI355X: pairing rows cost 5-10%).
+//
+// Mask variants (page "优化ScaledMaskSoftmax算子", the ScaledMaskSoftmax article): masked
+// scores count as minus infinity (section 2.1), a row with no kept element is zeros
+// (section 4.1), and section 6 builds window masks with tril, per-task masks broadcast over
+// the batch and per-sample length masks. The template parameter MK selects the kept set of
+// row r (valid length L; nothing is kept when r >= L):
+//   MK_TRIL  c <= r                                   (the grouped tril mask)
+//   MK_BAND  lo <= c - r <= hi, c < L                 (computed, never loaded)
+//   MK_MASK  mask[b, m, r, c] != 0, c < L             (one byte per element, loaded with
+//                                                      the scores; broadcast by strides)
+// In every case the kept columns lie in one interval [c0, c1] (Cols); only the vectors of
+// that interval are read, and everything outside it is written as zeros.
 #pragma once
 
 #include "device_common.h"
@@ -38,6 +50,7 @@
 namespace gtms {
 
 enum : unsigned { F_PAIR = 1u, F_XCD = 2u, F_LINES = 4u };
+enum : int { MK_TRIL = 0, MK_BAND = 1, MK_MASK = 2 };
 
 
 // Arguments of the forward (x -> y) and backward (y = x, upstream gradient g -> dx = y)
@@ -56,6 +69,9 @@ struct FwdArgs {
     float k;                   // forward: scale * log2(e); backward: scale
     unsigned flags;
     uint32_t xcd_shift;        // F_XCD: log2 of the blocks in one XCD chunk
+    int lo, hi;                // MK_BAND: kept when lo <= c - r <= hi (clamped to [-S, S])
+    const uint8_t* mask;       // MK_MASK: element (b, m, r, c) at mask[b*sb + m*sm + r*sr + c]
+    int64_t mask_sb, mask_sm, mask_sr;
 };
 
 struct Unit {
@@ -76,6 +92,33 @@ __device__ __forceinline__ const char* row_ptr(const void* base, uint32_t plane,
                                                const FwdArgs& a) {
     return (const char*)base +
            ((uint64_t)plane * (uint64_t)a.S + (uint64_t)r) * (uint64_t)a.row_bytes;
+}
+
+// Valid length of the plane's batch: seq_lens[b] clamped to [0, S], or S without lengths
+// (the mask variants accept none).
+template <int MK>
+__device__ __forceinline__ int valid_len(const FwdArgs& a, uint32_t plane) {
+    if (MK != MK_TRIL && !a.seq_lens) return a.S;
+    return clamp_len(a.seq_lens[plane / a.M], a.S);
+}
+
+// The interval [c0, c1] of columns that may be kept in row r; empty when c1 < c0.
+struct Cols {
+    int c0, c1;
+    __device__ __forceinline__ bool empty() const { return c1 < c0; }
+};
+
+template <int MK>
+__device__ __forceinline__ Cols kept_cols(const FwdArgs& a, int r, int L) {
+    if (r >= L) return {0, -1};
+    if constexpr (MK == MK_TRIL) return {0, r};
+    else if constexpr (MK == MK_BAND) return {max(0, r + a.lo), min(L - 1, r + a.hi)};
+    else return {0, L - 1};
+}
+
+__device__ __forceinline__ const uint8_t* mask_row(const FwdArgs& a, uint32_t plane, int r) {
+    const uint32_t b = plane / a.M, m = plane - b * a.M;
+    return a.mask + (int64_t)b * a.mask_sb + (int64_t)m * a.mask_sm + (int64_t)r * a.mask_sr;
 }
 
 // Zeros into slots [FROM, TO) of a row held with stride STRIDE (slots past the row end are
@@ -107,12 +150,17 @@ struct Span {
     int hv;              // leading slots that belong to the previous row's tail zone
 };
 
-// Whether the last `zone` bytes of row r (valid length L) hold kept elements.
-__device__ __forceinline__ bool tail_zone_has_data(int r, int L, int S, int zone, int esize) {
-    return zone > 0 && r < L && r >= S - zone / esize;
+// Whether the last `zone` bytes of row r (valid length L) may hold kept elements (for an
+// explicit mask: whether they lie in the row's interval, whatever the mask bytes say).
+template <int MK>
+__device__ __forceinline__ bool tail_zone_has_data(const FwdArgs& a, int r, int L, int zone,
+                                                   int esize) {
+    if (zone == 0) return false;
+    const Cols k = kept_cols<MK>(a, r, L);
+    return !k.empty() && k.c1 >= a.S - zone / esize;
 }
 
-template <int ESIZE>
+template <int MK, int ESIZE>
 __device__ __forceinline__ Span row_span(const FwdArgs& a, uint32_t plane, int r, int L) {
     Span sp;
     const char* row = row_ptr(a.y, plane, r, a);
@@ -127,10 +175,10 @@ __device__ __forceinline__ Span row_span(const FwdArgs& a, uint32_t plane, int r
     if (head && !first) {
         bool prev_data;
         if (r > 0) {
-            prev_data = tail_zone_has_data(r - 1, L, a.S, head, ESIZE);
+            prev_data = tail_zone_has_data<MK>(a, r - 1, L, head, ESIZE);
         } else {
-            const int Lp = clamp_len(a.seq_lens[(plane - 1) / a.M], a.S);
-            prev_data = tail_zone_has_data(a.S - 1, Lp, a.S, head, ESIZE);
+            const int Lp = valid_len<MK>(a, plane - 1);
+            prev_data = tail_zone_has_data<MK>(a, a.S - 1, Lp, head, ESIZE);
         }
         if (!prev_data) {
             sp.out -= head;
@@ -138,7 +186,7 @@ __device__ __forceinline__ Span row_span(const FwdArgs& a, uint32_t plane, int r
             sp.hv = head / 16;
         }
     }
-    if (tail && !last && !tail_zone_has_data(r, L, a.S, tail, ESIZE)) sp.out_bytes -= tail;
+    if (tail && !last && !tail_zone_has_data<MK>(a, r, L, tail, ESIZE)) sp.out_bytes -= tail;
     return sp;
 }
 
@@ -155,37 +203,53 @@ __device__ __forceinline__ Span row_span(const FwdArgs& a, uint32_t plane, int r
 // so each element costs one exp. A thread without kept columns has m_t = -inf, s_t = 0.
 constexpr int kOutOfRange = (int)0x80000000u;  // an offset every buffer range check rejects
 
-template <class IO, int NA, int STRIDE>
+template <class IO, int NA, int STRIDE, int MK>
 struct RowPart {
+    using MIO = MaskIo<IO::VEC>;
     typename IO::raw_t raw[NA];
+    typename MIO::raw_t mk[MK == MK_MASK ? NA : 1];
     float e[NA][IO::VEC];
     float m, s;
 
-    // kept elements of the vector in slot j: elements q < kc are kept
-    __device__ __forceinline__ static int kept_count(int t, int j, int hv, int r) {
+    // Element q of the vector in slot j is kept when its column c = v*VEC + q lies in
+    // [c0, c1] (and, for an explicit mask, its mask byte is non-zero): q >= ka and q < kc.
+    __device__ __forceinline__ static int kept_count(int t, int j, int hv, const Cols& k) {
         const int v = t + j * STRIDE - hv;
-        return v < 0 ? 0 : r + 1 - v * IO::VEC;
+        return v < 0 ? 0 : k.c1 + 1 - v * IO::VEC;
+    }
+    __device__ __forceinline__ static int kept_from(int t, int j, int hv, const Cols& k) {
+        return MK == MK_TRIL ? 0 : k.c0 - (t + j * STRIDE - hv) * IO::VEC;
+    }
+    __device__ __forceinline__ bool kept(int j, int q, int ka, int kc) const {
+        bool r = q < kc && (MK == MK_TRIL || q >= ka);
+        if constexpr (MK == MK_MASK) r = r && MIO::kept(mk[j], q);
+        return r;
     }
 
-    __device__ __forceinline__ void load(rsrc_t in, int t, int hv) {
+    // Vectors before the interval (and the previous row's zone, v < 0) are not fetched.
+    __device__ __forceinline__ void load(rsrc_t in, rsrc_t min, int t, int hv, const Cols& k) {
+        const int v0 = MK == MK_TRIL ? 0 : k.c0 / IO::VEC;
 #pragma unroll
         for (int j = 0; j < NA; ++j) {
             const int v = t + j * STRIDE - hv;
-            raw[j] = IO::template load<kPolicyDefault>(in, v < 0 ? kOutOfRange : v * IO::BYTES);
+            const bool skip = v < v0;
+            raw[j] = IO::template load<kPolicyDefault>(in, skip ? kOutOfRange : v * IO::BYTES);
+            if constexpr (MK == MK_MASK)
+                mk[j] = MIO::load(min, skip ? kOutOfRange : v * IO::VEC);
         }
     }
 
-    __device__ __forceinline__ void compute(int t, int hv, int r, float k) {
+    __device__ __forceinline__ void compute(int t, int hv, const Cols& k, float kscale) {
         constexpr int VEC = IO::VEC;
         m = -INFINITY;
 #pragma unroll
         for (int j = 0; j < NA; ++j) {
-            const int kc = kept_count(t, j, hv, r);
+            const int kc = kept_count(t, j, hv, k), ka = kept_from(t, j, hv, k);
             float f[VEC];
             IO::unpack(raw[j], f);
 #pragma unroll
             for (int q = 0; q < VEC; ++q) {
-                e[j][q] = q < kc ? f[q] * k : -INFINITY;
+                e[j][q] = kept(j, q, ka, kc) ? f[q] * kscale : -INFINITY;
                 m = fmaxf(m, e[j][q]);
             }
         }
@@ -206,7 +270,9 @@ struct RowPart {
         return m == -INFINITY ? 0.0f : s * __builtin_amdgcn_exp2f(m - M);
     }
 
-    // Scale of this thread's e once the group max M and sum S are known.
+    // Scale of this thread's e once the group max M and sum S are known. A row whose kept
+    // set turns out empty (an explicit mask row of zeros) has S = 0 and every m = -inf:
+    // the gain is 0 and the row is written as zeros.
     __device__ __forceinline__ float gain(float M, float S) const {
         return m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M) / S;
     }
@@ -214,14 +280,15 @@ struct RowPart {
     // Writes slots 0..NA-1. The select keeps masked columns at +0 even when g is NaN (a
     // NaN among the kept scores).
     template <int SP>
-    __device__ __forceinline__ void write(rsrc_t out, int t, int hv, int r, float g) const {
+    __device__ __forceinline__ void write(rsrc_t out, int t, int hv, const Cols& k,
+                                          float g) const {
         constexpr int VEC = IO::VEC;
 #pragma unroll
         for (int j = 0; j < NA; ++j) {
-            const int kc = kept_count(t, j, hv, r);
+            const int kc = kept_count(t, j, hv, k), ka = kept_from(t, j, hv, k);
             float f[VEC];
 #pragma unroll
-            for (int q = 0; q < VEC; ++q) f[q] = q < kc ? e[j][q] * g : 0.0f;
+            for (int q = 0; q < VEC; ++q) f[q] = kept(j, q, ka, kc) ? e[j][q] * g : 0.0f;
             IO::template store<SP>(out, (t + j * STRIDE) * IO::BYTES, IO::pack(f));
         }
     }
@@ -239,32 +306,35 @@ __device__ __forceinline__ void with_live_slots(int na, F&& f) {
 }
 
 // --------------------------------------------------------------------------- fwd_wave
-template <int DT, bool WIDE, int NV, int SP>
+template <int DT, bool WIDE, int NV, int SP, int MK>
 __device__ __forceinline__ void wave_row(const FwdArgs& a, uint32_t plane, int r, int L,
                                          int lane) {
     using IO = Io<DT, WIDE>;
-    const Span sp = row_span<IO::BYTES / IO::VEC>(a, plane, r, L);
+    const Span sp = row_span<MK, IO::BYTES / IO::VEC>(a, plane, r, L);
     const rsrc_t out = make_rsrc(sp.out, sp.out_bytes);
-    if (r >= L) {
+    const Cols k = kept_cols<MK>(a, r, L);
+    if (k.empty()) {
         write_zero_slots<IO, 0, NV, kWave, SP>(out, lane);
         return;
     }
-    const int nin = r / IO::VEC + 1;  // natural vectors holding columns 0..r
+    const int nin = k.c1 / IO::VEC + 1;  // natural vectors holding columns 0..c1
     const rsrc_t in = make_rsrc(row_ptr(a.x, plane, r, a), (uint32_t)(nin * IO::BYTES));
+    const rsrc_t min = MK == MK_MASK ? make_rsrc(mask_row(a, plane, r), (uint32_t)(nin * IO::VEC))
+                                     : in;
     const int hv = sp.hv;
     with_live_slots<NV>((nin + hv + kWave - 1) / kWave, [&]<int NA>() {
-        RowPart<IO, NA, kWave> p;
-        p.load(in, lane, hv);
+        RowPart<IO, NA, kWave, MK> p;
+        p.load(in, min, lane, hv, k);
         write_zero_slots<IO, NA, NV, kWave, SP>(out, lane);
-        p.compute(lane, hv, r, a.k);
+        p.compute(lane, hv, k, a.k);
         const float M = wave_reduce<OpMax>(p.m);
         const float S = wave_reduce<OpSum>(p.sum_at(M));
-        p.template write<SP>(out, lane, hv, r, p.gain(M, S));
+        p.template write<SP>(out, lane, hv, k, p.gain(M, S));
     });
 }
 
 // WPB wavefronts per workgroup, each on its own unit (a row, or a row pair).
-template <int DT, bool WIDE, int NV, int WPB, int SP>
+template <int DT, bool WIDE, int NV, int WPB, int SP, int MK>
 __global__ __launch_bounds__(WPB * kWave) void fwd_wave(FwdArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t wave = WPB == 1 ? 0u : (uint32_t)uniform(threadIdx.x / kWave);
@@ -273,9 +343,9 @@ __global__ __launch_bounds__(WPB * kWave) void fwd_wave(FwdArgs a) {
     for (uint64_t unit = (uint64_t)blk * WPB + wave; unit < a.n_units;
          unit += (uint64_t)nblk * WPB) {
         const Unit u = decode_unit((uint32_t)unit, a);
-        const int L = clamp_len(a.seq_lens[u.plane / a.M], a.S);
-        wave_row<DT, WIDE, NV, SP>(a, u.plane, u.r0, L, lane);
-        if (u.r1 >= 0) wave_row<DT, WIDE, NV, SP>(a, u.plane, u.r1, L, lane);
+        const int L = valid_len<MK>(a, u.plane);
+        wave_row<DT, WIDE, NV, SP, MK>(a, u.plane, u.r0, L, lane);
+        if (u.r1 >= 0) wave_row<DT, WIDE, NV, SP, MK>(a, u.plane, u.r1, L, lane);
     }
 }
 
@@ -295,27 +365,30 @@ __device__ __forceinline__ void merge_partials(const float* pm, const float* ps,
         s += pm[w] == -INFINITY ? 0.0f : ps[w] * __builtin_amdgcn_exp2f(pm[w] - m);
 }
 
-template <int DT, bool WIDE, int NV, int W, int SP>
+template <int DT, bool WIDE, int NV, int W, int SP, int MK>
 __device__ __forceinline__ void block_row(const FwdArgs& a, uint32_t plane, int r, int L,
                                           float* pm, float* ps) {
     using IO = Io<DT, WIDE>;
     constexpr int T = W * kWave;
     const int t = threadIdx.x;
-    const Span sp = row_span<IO::BYTES / IO::VEC>(a, plane, r, L);
+    const Span sp = row_span<MK, IO::BYTES / IO::VEC>(a, plane, r, L);
     const rsrc_t out = make_rsrc(sp.out, sp.out_bytes);
-    if (r >= L) {  // uniform over the workgroup
+    const Cols k = kept_cols<MK>(a, r, L);
+    if (k.empty()) {  // uniform over the workgroup
         write_zero_slots<IO, 0, NV, T, SP>(out, t);
         return;
     }
     const int wave = uniform(t / kWave);
-    const int nin = r / IO::VEC + 1;
+    const int nin = k.c1 / IO::VEC + 1;
     const rsrc_t in = make_rsrc(row_ptr(a.x, plane, r, a), (uint32_t)(nin * IO::BYTES));
+    const rsrc_t min = MK == MK_MASK ? make_rsrc(mask_row(a, plane, r), (uint32_t)(nin * IO::VEC))
+                                     : in;
     const int hv = sp.hv;
     with_live_slots<NV>((nin + hv + T - 1) / T, [&]<int NA>() {
-        RowPart<IO, NA, T> p;
-        p.load(in, t, hv);
+        RowPart<IO, NA, T, MK> p;
+        p.load(in, min, t, hv, k);
         write_zero_slots<IO, NA, NV, T, SP>(out, t);
-        p.compute(t, hv, r, a.k);
+        p.compute(t, hv, k, a.k);
         // wave partials, then the workgroup merge through LDS
         const float mw = wave_reduce<OpMax>(p.m);
         const float sw = mw == -INFINITY ? 0.0f : wave_reduce<OpSum>(p.sum_at(mw));
@@ -326,20 +399,21 @@ __device__ __forceinline__ void block_row(const FwdArgs& a, uint32_t plane, int 
         __syncthreads();
         float M, S;
         merge_partials<W>(pm, ps, M, S);
-        p.template write<SP>(out, t, hv, r, p.gain(M, S));
+        p.template write<SP>(out, t, hv, k, p.gain(M, S));
     });
 }
 
-template <int DT, bool WIDE, int NV, int W, int SP>
+template <int DT, bool WIDE, int NV, int W, int SP, int MK>
 __global__ __launch_bounds__(W * kWave) void fwd_block(FwdArgs a) {
     __shared__ float part[2][2][W];  // [row of the unit][max, sum][wave]
     const uint32_t nblk = gridDim.x;
     const uint32_t blk = (a.flags & F_XCD) ? xcd_chunked(blockIdx.x, nblk, a.xcd_shift) : blockIdx.x;
     for (uint64_t unit = blk; unit < a.n_units; unit += nblk) {
         const Unit u = decode_unit((uint32_t)unit, a);
-        const int L = clamp_len(a.seq_lens[u.plane / a.M], a.S);
-        block_row<DT, WIDE, NV, W, SP>(a, u.plane, u.r0, L, part[0][0], part[0][1]);
-        if (u.r1 >= 0) block_row<DT, WIDE, NV, W, SP>(a, u.plane, u.r1, L, part[1][0], part[1][1]);
+        const int L = valid_len<MK>(a, u.plane);
+        block_row<DT, WIDE, NV, W, SP, MK>(a, u.plane, u.r0, L, part[0][0], part[0][1]);
+        if (u.r1 >= 0)
+            block_row<DT, WIDE, NV, W, SP, MK>(a, u.plane, u.r1, L, part[1][0], part[1][1]);
         __syncthreads();  // the next unit rewrites the partials
     }
 }
@@ -347,41 +421,54 @@ __global__ __launch_bounds__(W * kWave) void fwd_block(FwdArgs a) {
 // ------------------------------------------------------------------------- fwd_stream
 // Two passes over a row of any length. Pass 1 keeps a running (m, s) per thread, updated
 // per vector: m' = max(m, max of the vector), s' = s * 2^(m - m') + sum 2^(z - m'); the
-// wave and workgroup merges follow the same rule. Pass 2 re-reads the prefix and writes
-// 2^(z - m) / s. The zero tail is written first: it needs no data.
-template <int DT, bool WIDE, int W, int SP>
-__device__ __forceinline__ void stream_row(const char* xr, char* yr, int r, bool valid,
-                                           const FwdArgs& a, float* pm, float* ps) {
+// wave and workgroup merges follow the same rule. Pass 2 re-reads the interval and writes
+// 2^(z - m) / s. The zeros outside the interval are written first: they need no data.
+template <int DT, bool WIDE, int W, int SP, int MK>
+__device__ __forceinline__ void stream_row(const FwdArgs& a, uint32_t plane, int r, int L,
+                                           float* pm, float* ps) {
     using IO = Io<DT, WIDE>;
+    using MIO = MaskIo<IO::VEC>;
     constexpr int VEC = IO::VEC;
     constexpr int T = W * kWave;
     const int t = threadIdx.x;
     const int nraw = a.row_bytes / IO::BYTES;
-    const rsrc_t out = make_rsrc(yr, (uint32_t)a.row_bytes);
-    if (!valid) {
+    const rsrc_t out = make_rsrc(row_ptr(a.y, plane, r, a), (uint32_t)a.row_bytes);
+    const Cols k = kept_cols<MK>(a, r, L);
+    if (k.empty()) {
         for (int v = t; v < nraw; v += T)
             IO::template store<SP>(out, v * IO::BYTES, IO::zero());
         return;
     }
     const int wave = uniform(t / kWave);
-    const int nin = r / VEC + 1;
-    const rsrc_t in = make_rsrc(xr, (uint32_t)(nin * IO::BYTES));
+    const int v0 = k.c0 / VEC, nin = k.c1 / VEC + 1;
+    const rsrc_t in = make_rsrc(row_ptr(a.x, plane, r, a), (uint32_t)(nin * IO::BYTES));
+    const rsrc_t min = MK == MK_MASK ? make_rsrc(mask_row(a, plane, r), (uint32_t)(nin * VEC))
+                                     : in;
+    for (int v = t; v < v0; v += T) IO::template store<SP>(out, v * IO::BYTES, IO::zero());
     for (int v = nin + t; v < nraw; v += T)
         IO::template store<SP>(out, v * IO::BYTES, IO::zero());
+    auto kept = [&](int v, int e, const typename MIO::raw_t& mb) {
+        const int c = v * VEC + e;
+        bool r = c >= k.c0 && c <= k.c1;
+        if constexpr (MK == MK_MASK) r = r && MIO::kept(mb, e);
+        return r;
+    };
     float m = -INFINITY, s = 0.0f;
-    for (int v = t; v < nin; v += T) {
+    for (int v = v0 + t; v < nin; v += T) {
         float f[VEC];
         IO::unpack(IO::template load<kPolicyDefault>(in, v * IO::BYTES), f);
+        typename MIO::raw_t mb{};
+        if constexpr (MK == MK_MASK) mb = MIO::load(min, v * VEC);
         float vm = -INFINITY;
 #pragma unroll
         for (int e = 0; e < VEC; ++e)
-            if (v * VEC + e <= r) vm = fmaxf(vm, f[e] * a.k);
+            if (kept(v, e, mb)) vm = fmaxf(vm, f[e] * a.k);
         const float mn = fmaxf(m, vm);
         float add = 0.0f;
 #pragma unroll
         for (int e = 0; e < VEC; ++e)
-            add += v * VEC + e <= r ? __builtin_amdgcn_exp2f(f[e] * a.k - mn) : 0.0f;
-        s = (m == -INFINITY ? 0.0f : s * __builtin_amdgcn_exp2f(m - mn)) + add;
+            add += kept(v, e, mb) ? __builtin_amdgcn_exp2f(f[e] * a.k - mn) : 0.0f;
+        s = (mn == -INFINITY ? 0.0f : (m == -INFINITY ? 0.0f : s * __builtin_amdgcn_exp2f(m - mn)) + add);
         m = mn;
     }
     const float mw = wave_reduce<OpMax>(m);
@@ -394,32 +481,29 @@ __device__ __forceinline__ void stream_row(const char* xr, char* yr, int r, bool
     __syncthreads();
     float mt, st;
     merge_partials<W>(pm, ps, mt, st);
-    const float inv = 1.0f / st;
-    for (int v = t; v < nin; v += T) {
+    const float inv = mt == -INFINITY ? 0.0f : 1.0f / st;  // an explicit mask row of zeros
+    for (int v = v0 + t; v < nin; v += T) {
         float f[VEC];
         IO::unpack(IO::template load<kPolicyDefault>(in, v * IO::BYTES), f);
+        typename MIO::raw_t mb{};
+        if constexpr (MK == MK_MASK) mb = MIO::load(min, v * VEC);
 #pragma unroll
         for (int e = 0; e < VEC; ++e)
-            f[e] = v * VEC + e <= r ? __builtin_amdgcn_exp2f(f[e] * a.k - mt) * inv : 0.0f;
+            f[e] = kept(v, e, mb) ? __builtin_amdgcn_exp2f(f[e] * a.k - mt) * inv : 0.0f;
         IO::template store<SP>(out, v * IO::BYTES, IO::pack(f));
     }
 }
 
-template <int DT, bool WIDE, int W, int SP>
+template <int DT, bool WIDE, int W, int SP, int MK>
 __global__ __launch_bounds__(W * kWave) void fwd_stream(FwdArgs a) {
     __shared__ float part[2][2][W];
     const uint32_t nblk = gridDim.x;
     const uint32_t blk = (a.flags & F_XCD) ? xcd_chunked(blockIdx.x, nblk, a.xcd_shift) : blockIdx.x;
     for (uint64_t unit = blk; unit < a.n_units; unit += nblk) {
         const Unit u = decode_unit((uint32_t)unit, a);
-        const int L = clamp_len(a.seq_lens[u.plane / a.M], a.S);
-        stream_row<DT, WIDE, W, SP>(row_ptr(a.x, u.plane, u.r0, a),
-                                (char*)row_ptr(a.y, u.plane, u.r0, a), u.r0, u.r0 < L, a,
-                                part[0][0], part[0][1]);
-        if (u.r1 >= 0)
-            stream_row<DT, WIDE, W, SP>(row_ptr(a.x, u.plane, u.r1, a),
-                                    (char*)row_ptr(a.y, u.plane, u.r1, a), u.r1, u.r1 < L, a,
-                                    part[1][0], part[1][1]);
+        const int L = valid_len<MK>(a, u.plane);
+        stream_row<DT, WIDE, W, SP, MK>(a, u.plane, u.r0, L, part[0][0], part[0][1]);
+        if (u.r1 >= 0) stream_row<DT, WIDE, W, SP, MK>(a, u.plane, u.r1, L, part[1][0], part[1][1]);
         __syncthreads();
     }
 }

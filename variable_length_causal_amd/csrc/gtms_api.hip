@@ -5,18 +5,11 @@
 #include <string.h>
 
 #include "gtms.h"
-#include "backward_kernels.h"
-#include "forward_kernels.h"
+#include "launch.h"
 
 namespace gtms {
 namespace {
 
-constexpr int kMaxNV = 16;      // register-held vectors per lane
-constexpr int kAutoNV = 4;      // vectors per lane the automatic choice aims for
-constexpr int kWaveWPB = 4;     // wavefronts per workgroup on the wave path
-constexpr int kMaxW = 16;       // wavefronts per workgroup on the block path, at most
-constexpr int kStreamW = 8;     // wavefronts per workgroup on the stream path
-constexpr int64_t kMaxGrid = int64_t(1) << 22;
 // Each XCD takes chunks of 2^4 consecutive blocks (unless GTMS_FLAG_PLAIN_ORDER). Measured on
 // MI355X over chunk sizes of 1 to 4096 blocks: 16 was fastest on every workload and path
 // (binary32 rows of 1000 elements four to a block, 16-bit rows of 4096 and 8192 elements one
@@ -34,8 +27,8 @@ int64_t pow2_at_least(int64_t n) {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Shared argument checks; on success fills the byte count of one [B, M, S, S] tensor.
-int check_common(const void* a, const void* b, const int32_t* seq_lens, int64_t B, int64_t M,
-                 int64_t S, int dtype, int64_t* bytes, bool* empty) {
+int check_common(const void* a, const void* b, const int32_t* seq_lens, bool lens_optional,
+                 int64_t B, int64_t M, int64_t S, int dtype, int64_t* bytes, bool* empty) {
     if (dtype != GTMS_F32 && dtype != GTMS_F16 && dtype != GTMS_BF16) return GTMS_ERR_DTYPE;
     if (B < 0 || M < 0 || S < 0 || S > GTMS_MAX_S || M > INT32_MAX) return GTMS_ERR_INVALID_ARG;
     int64_t n = esize_of(dtype);
@@ -45,7 +38,7 @@ int check_common(const void* a, const void* b, const int32_t* seq_lens, int64_t 
     *bytes = n;
     *empty = (n == 0);
     if (*empty) return GTMS_OK;
-    if (!a || !b || !seq_lens) return GTMS_ERR_INVALID_ARG;
+    if (!a || !b || (!seq_lens && !lens_optional)) return GTMS_ERR_INVALID_ARG;
     const uintptr_t es = (uintptr_t)esize_of(dtype);
     if ((uintptr_t)a % es || (uintptr_t)b % es || (uintptr_t)seq_lens % 4) return GTMS_ERR_ALIGN;
     return GTMS_OK;
@@ -56,13 +49,6 @@ bool overlap_partial(const void* a, const void* b, int64_t bytes) {
     if (x == y) return false;
     return x < y + (uintptr_t)bytes && y < x + (uintptr_t)bytes;
 }
-
-struct Plan {
-    int path;  // GTMS_PATH_WAVE / BLOCK / STREAM
-    bool wide;
-    int nv;    // vectors per lane (wave, block)
-    int w;     // wavefronts per row (block, stream)
-};
 
 // Leading slots a row may take over from the previous row under line ownership: rows
 // start at base + k * row_bytes, so on a 128-byte aligned tensor the previous row's tail
@@ -121,103 +107,28 @@ int make_plan(int64_t S, int dtype, bool wide, int64_t slack, int path, Plan* p)
     }
 }
 
-// ----------------------------------------------------------------- launch by template
-unsigned grid_for(int64_t units, int64_t per_block) {
-    const int64_t blocks = cdiv(units, per_block);
-    return (unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid);
-}
-
-// OP selects the kernel family: forward (x -> y) or backward (y, g -> dx).
-enum : int { OP_FWD = 0, OP_BWD = 1 };
-
-template <int OP, int DT, bool WIDE, int NV>
-hipError_t launch_wave(const FwdArgs& a, hipStream_t st) {
-    const dim3 grid(grid_for(a.n_units, kWaveWPB)), block(kWaveWPB * kWave);
-    if constexpr (OP == OP_FWD)
-        hipLaunchKernelGGL((fwd_wave<DT, WIDE, NV, kWaveWPB, kPolicyStream>), grid, block, 0, st, a);
-    else
-        hipLaunchKernelGGL((bwd_wave<DT, WIDE, NV, kWaveWPB, kPolicyStream>), grid, block, 0, st, a);
-    return hipGetLastError();
-}
-
-template <int OP, int DT, bool WIDE, int NV, int W>
-hipError_t launch_block(const FwdArgs& a, hipStream_t st) {
-    const dim3 grid(grid_for(a.n_units, 1)), block(W * kWave);
-    if constexpr (OP == OP_FWD)
-        hipLaunchKernelGGL((fwd_block<DT, WIDE, NV, W, kPolicyStream>), grid, block, 0, st, a);
-    else
-        hipLaunchKernelGGL((bwd_block<DT, WIDE, NV, W, kPolicyStream>), grid, block, 0, st, a);
-    return hipGetLastError();
-}
-
-template <int OP, int DT, bool WIDE>
-hipError_t launch_stream(const FwdArgs& a, hipStream_t st) {
-    const dim3 grid(grid_for(a.n_units, 1)), block(kStreamW * kWave);
-    if constexpr (OP == OP_FWD)
-        hipLaunchKernelGGL((fwd_stream<DT, WIDE, kStreamW, kPolicyStream>), grid, block, 0, st, a);
-    else
-        hipLaunchKernelGGL((bwd_stream<DT, WIDE, kStreamW, kPolicyStream>), grid, block, 0, st, a);
-    return hipGetLastError();
-}
-
-template <int OP, int DT, bool WIDE, int W>
-hipError_t block_nv_small(int nv, const FwdArgs& a, hipStream_t st) {
-    switch (nv) {
-        case 1: return launch_block<OP, DT, WIDE, 1, W>(a, st);
-        case 2: return launch_block<OP, DT, WIDE, 2, W>(a, st);
-        case 4: return launch_block<OP, DT, WIDE, 4, W>(a, st);
-        default: return hipErrorInvalidValue;
-    }
-}
-
-template <int OP, int DT, bool WIDE>
-hipError_t dispatch_wide(const Plan& p, const FwdArgs& a, hipStream_t st) {
-    switch (p.path) {
-        case GTMS_PATH_STREAM:
-            return launch_stream<OP, DT, WIDE>(a, st);
-        case GTMS_PATH_WAVE:
-            switch (p.nv) {
-                case 1: return launch_wave<OP, DT, WIDE, 1>(a, st);
-                case 2: return launch_wave<OP, DT, WIDE, 2>(a, st);
-                case 4: return launch_wave<OP, DT, WIDE, 4>(a, st);
-                case 8: return launch_wave<OP, DT, WIDE, 8>(a, st);
-                case 16: return launch_wave<OP, DT, WIDE, 16>(a, st);
-                default: return hipErrorInvalidValue;
-            }
-        default:  // block
-            switch (p.w) {
-                case 2: return block_nv_small<OP, DT, WIDE, 2>(p.nv, a, st);
-                case 4: return block_nv_small<OP, DT, WIDE, 4>(p.nv, a, st);
-                case 8: return block_nv_small<OP, DT, WIDE, 8>(p.nv, a, st);
-                default:
-                    switch (p.nv) {
-                        case 1: return launch_block<OP, DT, WIDE, 1, 16>(a, st);
-                        case 2: return launch_block<OP, DT, WIDE, 2, 16>(a, st);
-                        case 4: return launch_block<OP, DT, WIDE, 4, 16>(a, st);
-                        case 8: return launch_block<OP, DT, WIDE, 8, 16>(a, st);
-                        case 16: return launch_block<OP, DT, WIDE, 16, 16>(a, st);
-                        default: return hipErrorInvalidValue;
-                    }
-            }
-    }
-}
-
-template <int OP, int DT>
-hipError_t dispatch(const Plan& p, const FwdArgs& a, hipStream_t st) {
-    return p.wide ? dispatch_wide<OP, DT, true>(p, a, st) : dispatch_wide<OP, DT, false>(p, a, st);
-}
+// Which elements a call keeps (beyond r < L, c < L): MK_TRIL c <= r; MK_BAND
+// lo <= c - r <= hi; MK_MASK a non-zero byte of `mask` (byte strides sb, sm, sr).
+struct MaskSpec {
+    int kind = MK_TRIL;
+    int64_t lo = 0, hi = 0;
+    const uint8_t* mask = nullptr;
+    int64_t sb = 0, sm = 0, sr = 0;
+};
 
 // Shared body of the forward (x -> out) and backward (x = y, g = dy -> out = dx) calls.
 template <int OP>
 int run_impl(const void* x, const void* g, void* out, const int32_t* seq_lens, int64_t B,
              int64_t M, int64_t S, float scale, int dtype, int path, unsigned flags,
-             void* stream) {
+             void* stream, const MaskSpec& mk = MaskSpec()) {
     int64_t bytes;
     bool empty;
-    int st = check_common(x, out, seq_lens, B, M, S, dtype, &bytes, &empty);
+    int st = check_common(x, out, seq_lens, mk.kind != MK_TRIL, B, M, S, dtype, &bytes, &empty);
     if (st != GTMS_OK) return st;
     if (path < GTMS_PATH_AUTO || path > GTMS_PATH_STREAM) return GTMS_ERR_PATH;
+    if (mk.kind == MK_MASK && (mk.sb < 0 || mk.sm < 0 || mk.sr < 0)) return GTMS_ERR_INVALID_ARG;
     if (empty) return GTMS_OK;
+    if (mk.kind == MK_MASK && !mk.mask) return GTMS_ERR_INVALID_ARG;
     if (OP == OP_BWD) {
         if (!g) return GTMS_ERR_INVALID_ARG;
         if ((uintptr_t)g % esize_of(dtype)) return GTMS_ERR_ALIGN;
@@ -229,8 +140,13 @@ int run_impl(const void* x, const void* g, void* out, const int32_t* seq_lens, i
     }
 
     const int vec = 16 / esize_of(dtype);
+    // 16-byte vectors need aligned rows of scores and, for an explicit mask, mask rows
+    // whose VEC bytes per vector sit at multiples of VEC
+    const bool mask_wide = mk.kind != MK_MASK ||
+                           ((uintptr_t)mk.mask % vec == 0 && mk.sb % vec == 0 &&
+                            mk.sm % vec == 0 && mk.sr % vec == 0);
     const bool wide = S % vec == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)out % 16 == 0 &&
-                      (OP == OP_FWD || (uintptr_t)g % 16 == 0);
+                      (OP == OP_FWD || (uintptr_t)g % 16 == 0) && mask_wide;
     // whole-line writes at row boundaries (wave and block paths, rows of 16-byte vectors)
     const int64_t row_bytes = S * esize_of(dtype);
     const bool lines = wide && row_bytes >= 128 && path != GTMS_PATH_STREAM;
@@ -258,15 +174,40 @@ int run_impl(const void* x, const void* g, void* out, const int32_t* seq_lens, i
     a.n_planes = (uint32_t)(B * M);
     // forward: scale * log2(e), so that exp is 2^x; backward: the scale itself
     a.k = OP == OP_FWD ? (float)((double)scale * 1.4426950408889634074) : scale;
+    // c - r lies in [-(S-1), S-1], so clamping the band to [-S, S] changes nothing
+    a.lo = (int)(mk.lo < -S ? -S : (mk.lo > S ? S : mk.lo));
+    a.hi = (int)(mk.hi < -S ? -S : (mk.hi > S ? S : mk.hi));
+    a.mask = mk.mask;
+    a.mask_sb = mk.sb;
+    a.mask_sm = mk.sm;
+    a.mask_sr = mk.sr;
 
     hipStream_t hs = (hipStream_t)stream;
     hipError_t e;
-    switch (dtype) {
-        case GTMS_F32: e = dispatch<OP, DT_F32>(plan, a, hs); break;
-        case GTMS_F16: e = dispatch<OP, DT_F16>(plan, a, hs); break;
-        default: e = dispatch<OP, DT_BF16>(plan, a, hs); break;
+    switch (mk.kind) {
+        case MK_TRIL: e = launch_kind<OP, MK_TRIL>(dtype, plan, a, hs); break;
+        case MK_BAND: e = launch_kind<OP, MK_BAND>(dtype, plan, a, hs); break;
+        default: e = launch_kind<OP, MK_MASK>(dtype, plan, a, hs); break;
     }
     return e == hipSuccess ? GTMS_OK : GTMS_ERR_HIP;
+}
+
+MaskSpec band(int64_t lo, int64_t hi) {
+    MaskSpec m;
+    m.kind = MK_BAND;
+    m.lo = lo;
+    m.hi = hi;
+    return m;
+}
+
+MaskSpec explicit_mask(const uint8_t* mask, int64_t sb, int64_t sm, int64_t sr) {
+    MaskSpec m;
+    m.kind = MK_MASK;
+    m.mask = mask;
+    m.sb = sb;
+    m.sm = sm;
+    m.sr = sr;
+    return m;
 }
 
 }  // namespace
@@ -300,6 +241,53 @@ int gtms_backward_ex(const void* y, const void* dy, void* dx, const int32_t* seq
                                         stream);
 }
 
+int gtms_forward_band(const void* in, void* out, const int32_t* seq_lens, int64_t B,
+                      int64_t M, int64_t S, int64_t lo, int64_t hi, float scale, int dtype,
+                      void* stream) {
+    return gtms::run_impl<gtms::OP_FWD>(in, nullptr, out, seq_lens, B, M, S, scale, dtype,
+                                        GTMS_PATH_AUTO, 0u, stream, gtms::band(lo, hi));
+}
+
+int gtms_forward_band_ex(const void* in, void* out, const int32_t* seq_lens, int64_t B,
+                         int64_t M, int64_t S, int64_t lo, int64_t hi, float scale, int dtype,
+                         int path, unsigned flags, void* stream) {
+    return gtms::run_impl<gtms::OP_FWD>(in, nullptr, out, seq_lens, B, M, S, scale, dtype, path,
+                                        flags, stream, gtms::band(lo, hi));
+}
+
+int gtms_forward_masked(const void* in, void* out, const uint8_t* mask, int64_t mask_stride_b,
+                        int64_t mask_stride_m, int64_t mask_stride_r, const int32_t* seq_lens,
+                        int64_t B, int64_t M, int64_t S, float scale, int dtype, void* stream) {
+    return gtms::run_impl<gtms::OP_FWD>(
+        in, nullptr, out, seq_lens, B, M, S, scale, dtype, GTMS_PATH_AUTO, 0u, stream,
+        gtms::explicit_mask(mask, mask_stride_b, mask_stride_m, mask_stride_r));
+}
+
+int gtms_forward_masked_ex(const void* in, void* out, const uint8_t* mask,
+                           int64_t mask_stride_b, int64_t mask_stride_m, int64_t mask_stride_r,
+                           const int32_t* seq_lens, int64_t B, int64_t M, int64_t S,
+                           float scale, int dtype, int path, unsigned flags, void* stream) {
+    return gtms::run_impl<gtms::OP_FWD>(
+        in, nullptr, out, seq_lens, B, M, S, scale, dtype, path, flags, stream,
+        gtms::explicit_mask(mask, mask_stride_b, mask_stride_m, mask_stride_r));
+}
+
+int gtms_backward_band(const void* y, const void* dy, void* dx, const int32_t* seq_lens,
+                       int64_t B, int64_t M, int64_t S, int64_t lo, int64_t hi, float scale,
+                       int dtype, int path, unsigned flags, void* stream) {
+    return gtms::run_impl<gtms::OP_BWD>(y, dy, dx, seq_lens, B, M, S, scale, dtype, path, flags,
+                                        stream, gtms::band(lo, hi));
+}
+
+int gtms_backward_masked(const void* y, const void* dy, void* dx, const uint8_t* mask,
+                         int64_t mask_stride_b, int64_t mask_stride_m, int64_t mask_stride_r,
+                         const int32_t* seq_lens, int64_t B, int64_t M, int64_t S, float scale,
+                         int dtype, int path, unsigned flags, void* stream) {
+    return gtms::run_impl<gtms::OP_BWD>(
+        y, dy, dx, seq_lens, B, M, S, scale, dtype, path, flags, stream,
+        gtms::explicit_mask(mask, mask_stride_b, mask_stride_m, mask_stride_r));
+}
+
 const char* gtms_status_string(int status) {
     switch (status) {
         case GTMS_OK: return "ok";
@@ -312,6 +300,6 @@ const char* gtms_status_string(int status) {
     }
 }
 
-int gtms_version(void) { return 100; }
+int gtms_version(void) { return 200; }
 
 }  // extern "C"
