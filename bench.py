@@ -11,6 +11,12 @@ Prints ONE JSON line. value = effective HBM throughput over the algorithmic byte
 step: the kept lower-triangle reads plus the full S*S writes,
     bytes = esize * (sum_b M * L_b (L_b + 1) / 2 + B * M * S^2)
 (--op backward: gtms_backward instead, reading two kept triangles, y and dy).
+--variant band / mask measure the mask variants of the ScaledMaskSoftmax article instead:
+a band lo <= c - r <= hi (default: a causal window of 512 columns), or an explicit byte
+mask (default: the article's window mask tril(w), one [S, S] mask shared by every plane).
+Their bytes count the reads of each row's column interval (the band itself; [0, L_b - 1]
+for an explicit mask, which the kernel cannot narrow without reading the mask), the mask's
+own bytes once, and the full writes.
 The roofline object reports the same bytes over the kernel's average duration measured
 with HIP events on the launch stream, against the 8 TB/s HBM peak of the MI355X. The
 cpu_baseline object times the fp64 CPU oracle on the same workload on the host.
@@ -36,7 +42,7 @@ METRIC = "ms and effective HBM GB/s (% of peak) for [B,M,S,S] masked softmax"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "variable_length_causal_amd", "csrc", f)
                   for f in ("device_common.h", "forward_kernels.h", "backward_kernels.h",
-                            "gtms_api.hip")]
+                            "gtms_api.hip", "launch.h", "launch_kind.hip")]
 
 
 def algorithmic_bytes(w: workloads.Workload, lens, op: str = "forward") -> int:
@@ -45,6 +51,26 @@ def algorithmic_bytes(w: workloads.Workload, lens, op: str = "forward") -> int:
     reads = sum(w.M * min(max(int(L), 0), S) * (min(max(int(L), 0), S) + 1) // 2 for L in lens)
     writes = w.B * w.M * S * S
     return w.esize * ((2 if op == "backward" else 1) * reads + writes)
+
+
+def variant_bytes(w: workloads.Workload, lens, variant: str, lo: int, hi: int,
+                  op: str = "forward", mask_bytes: int = 0) -> int:
+    """Algorithmic bytes of a mask variant: interval reads (x forward; y and dy backward),
+    the mask's bytes once, full writes."""
+    S = w.S
+    reads = 0
+    for L in lens:
+        Lc = min(max(int(L), 0), S)
+        if variant == "band":
+            r = np.arange(Lc)
+            c0 = np.maximum(0, r + lo)
+            c1 = np.minimum(Lc - 1, r + hi)
+            reads += int(np.maximum(c1 - c0 + 1, 0).sum())
+        else:
+            reads += Lc * Lc
+    reads *= w.M
+    writes = w.B * w.M * S * S
+    return w.esize * ((2 if op == "backward" else 1) * reads + writes) + mask_bytes
 
 
 def kernel_sources_hash() -> str:
@@ -110,6 +136,11 @@ def main():
                     choices=sorted(k for k in workloads.WORKLOADS if "example" not in k))
     ap.add_argument("--op", default="forward", choices=["forward", "backward"],
                     help="the forward (the headline) or its backward")
+    ap.add_argument("--variant", default="tril", choices=["tril", "band", "mask"],
+                    help="the grouped tril mask (the headline), a band, or an explicit mask")
+    ap.add_argument("--band", default="-511,0",
+                    help="band: lo,hi (kept when lo <= c - r <= hi); mask: hi = the w of "
+                         "the window mask tril(w)")
     ap.add_argument("--path", default="auto", choices=["auto", "wave", "block", "stream"])
     ap.add_argument("--flags", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -135,7 +166,16 @@ def main():
     w = workloads.WORKLOADS[args.workload]
     lens = workloads.seq_lens(w)
     sl = torch.as_tensor(lens).to(dev)
-    step_bytes = algorithmic_bytes(w, lens, args.op)
+    lo, hi = (int(v) for v in args.band.split(","))
+    mask = None
+    if args.variant == "mask":  # the window mask tril(w): kept where c - r <= hi
+        mask = torch.ones(w.S, w.S, dtype=torch.uint8, device=dev).tril(hi)[None, None]
+        lo = -w.S
+    if args.variant == "tril":
+        step_bytes = algorithmic_bytes(w, lens, args.op)
+    else:
+        step_bytes = variant_bytes(w, lens, args.variant, lo, hi, args.op,
+                                   0 if mask is None else mask.numel())
     tensor_bytes = w.B * w.M * w.S * w.S * w.esize
 
     # rotate over enough (input, output) pairs that consecutive uses of one pair are
@@ -149,17 +189,33 @@ def main():
     gs = []
     if args.op == "backward":
         for i in range(nsets):  # y = the forward's output, dy = normal
-            g.forward(xs[i], sl, w.scale, out=ys[i])
+            if args.variant == "band":
+                g.forward_band(xs[i], sl, lo, hi, w.scale, out=ys[i])
+            elif args.variant == "mask":
+                g.forward_masked(xs[i], mask, sl, w.scale, out=ys[i])
+            else:
+                g.forward(xs[i], sl, w.scale, out=ys[i])
             gs.append(workloads.scores_device(w.shape, w.dtype, 1.0, w.x_seed + 100 + i, dev))
     torch.cuda.synchronize()
 
     def step(i):
+        x, y = xs[i % nsets], ys[i % nsets]
         if args.op == "backward":
-            g.backward(ys[i % nsets], gs[i % nsets], sl, w.scale, out=xs[i % nsets],
-                       path=args.path, flags=args.flags)
+            dy = gs[i % nsets]
+            if args.variant == "band":
+                g.backward_band(y, dy, sl, lo, hi, w.scale, out=x, path=args.path,
+                                flags=args.flags)
+            elif args.variant == "mask":
+                g.backward_masked(y, dy, mask, sl, w.scale, out=x, path=args.path,
+                                  flags=args.flags)
+            else:
+                g.backward(y, dy, sl, w.scale, out=x, path=args.path, flags=args.flags)
+        elif args.variant == "band":
+            g.forward_band(x, sl, lo, hi, w.scale, out=y, path=args.path, flags=args.flags)
+        elif args.variant == "mask":
+            g.forward_masked(x, mask, sl, w.scale, out=y, path=args.path, flags=args.flags)
         else:
-            g.forward(xs[i % nsets], sl, w.scale, out=ys[i % nsets], path=args.path,
-                      flags=args.flags)
+            g.forward(x, sl, w.scale, out=y, path=args.path, flags=args.flags)
 
     for i in range(args.warmup):
         step(i)
@@ -200,8 +256,9 @@ def main():
 
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = step_bytes / (avg_kernel_ms * 1e-3) / 1e9
-    traffic = measured_traffic(args.workload if args.op == "forward" else
-                               f"{args.workload}:backward")
+    key = args.workload + ("" if args.op == "forward" else ":backward") + \
+        ("" if args.variant == "tril" else f":{args.variant}{lo},{hi}")
+    traffic = measured_traffic(key)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -218,6 +275,8 @@ def main():
         "config": {
             "workload": w.name,
             "op": args.op,
+            "variant": args.variant if args.variant == "tril" else
+            (f"band lo={lo} hi={hi}" if args.variant == "band" else f"mask tril({hi}) [1,1,S,S]"),
             "B": w.B, "M": w.M, "S": w.S,
             "seq_lens": [int(v) for v in lens],
             "scale": w.scale,
@@ -236,7 +295,7 @@ def main():
         },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline and args.op == "forward":
+    if not args.no_cpu_baseline and args.op == "forward" and args.variant == "tril":
         out["cpu_baseline"] = cpu_baseline(xs[0], lens, w, args.cpu_budget)
     print(json.dumps(out), flush=True)
 
