@@ -93,6 +93,8 @@ class Oracle:
         lib.gtms_oracle_masked_backward_f64.argtypes = [p, p, p, p, i64, i64, i64, p, i64, i64,
                                                         i64, f32, i32]
         lib.gtms_oracle_masked_backward_f64.restype = i32
+        lib.gtms_oracle_attention_f64.argtypes = [p, p, p, p, p, i64, i64, i64, i64, f32, i32]
+        lib.gtms_oracle_attention_f64.restype = i32
         lib.gtms_oracle_decode.argtypes = [ctypes.c_uint32, i32]
         lib.gtms_oracle_decode.restype = ctypes.c_double
         lib.gtms_oracle_encode.argtypes = [ctypes.c_double, i32]
@@ -218,6 +220,19 @@ class Oracle:
                      "gtms_oracle_masked_backward_f64")
         return dx
 
+    def attention_f64(self, q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_lens,
+                      scale: float, dtype: int = F32) -> np.ndarray:
+        """fp64 attention output [B, M, S, D] with the grouped tril mask (raw storage in)."""
+        q, k, v = _check(q, dtype), _check(k, dtype), _check(v, dtype)
+        B, M, S, D = q.shape
+        assert k.shape == q.shape and v.shape == q.shape
+        sl = _lens(seq_lens, B)
+        o = np.empty(q.shape, dtype=np.float64)
+        self._status(self.lib.gtms_oracle_attention_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                                        _ptr(sl), B, M, S, D, scale, dtype),
+                     "gtms_oracle_attention_f64")
+        return o
+
     def decode(self, bits: int, dtype: int) -> float:
         return self.lib.gtms_oracle_decode(int(bits), dtype)
 
@@ -284,3 +299,7 @@ def softmax_masked_f64(*a, **k):
 
 def masked_backward_f64(*a, **k):
     return default().masked_backward_f64(*a, **k)
+
+
+def attention_f64(*a, **k):
+    return default().attention_f64(*a, **k)

@@ -450,3 +450,59 @@ int gtms_oracle_masked_backward_f64(const void* y, const void* dy, double* dx,
     return run_variant(y, dy, dx, mask, mask_sb, mask_sm, mask_sr, 0, 0, seq_lens, B, M, S,
                        scale, dtype);
 }
+
+/* ------------------------------------------------------------------------------------
+ * Attention with the grouped tril mask. The self-attention article ("ops(8) self-attention
+ * CUDA", sections 1 and 2) computes attention as three steps: scores S = Q K^T, a softmax
+ * of each score row, and O = P V. Here the softmax is this operation's: for batch b with
+ * valid length L (clamped to [0, S]) and query row r < L, the row keeps the keys c <= r,
+ * and
+ *   O[r] = sum_{c <= r} p_c V[c],  p_c = exp(z_c - mu) / sum_{k <= r} exp(z_k - mu),
+ *   z_c = scale * sum_d Q[r, d] K[c, d],
+ * while a query row r >= L is all zeros (a padded row of the softmax gives P = 0).
+ * Q, K, V and O are [B, M, S, D], row-major, in the element type; out receives fp64.
+ * ------------------------------------------------------------------------------------ */
+int gtms_oracle_attention_f64(const void* q, const void* k, const void* v, double* out,
+                              const int32_t* seq_lens, int64_t B, int64_t M, int64_t S,
+                              int64_t D, float scale, int dtype) {
+    int ebits, pbits, bytes;
+    if (!format_of(dtype, &ebits, &pbits, &bytes)) return ERR_DTYPE;
+    if (B < 0 || M < 0 || S < 0 || D < 0) return ERR_ARG;
+    int64_t n = 1;
+    if (__builtin_mul_overflow(n, B, &n) || __builtin_mul_overflow(n, M, &n) ||
+        __builtin_mul_overflow(n, S, &n) || __builtin_mul_overflow(n, D, &n))
+        return ERR_ARG;
+    if (n == 0) return OK;
+    if (!q || !k || !v || !out || !seq_lens) return ERR_ARG;
+    double* z = (double*)malloc((size_t)S * sizeof(double));
+    if (!z) return ERR_ARG;
+    for (int64_t b = 0; b < B; ++b) {
+        int64_t L = valid_length(seq_lens[b], S);
+        for (int64_t m = 0; m < M; ++m) {
+            int64_t head = (b * M + m) * S * D;  /* first element of this head's [S, D] */
+            for (int64_t r = 0; r < S; ++r) {
+                double* o = out + head + r * D;
+                for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+                if (r >= L) continue;
+                /* scores of the kept keys c = 0..r and their maximum */
+                double mu = -INFINITY;
+                for (int64_t c = 0; c <= r; ++c) {
+                    double dot = 0.0;
+                    for (int64_t d = 0; d < D; ++d)
+                        dot += load_elem(q, head + r * D + d, dtype) *
+                               load_elem(k, head + c * D + d, dtype);
+                    z[c] = (double)scale * dot;
+                    if (z[c] > mu) mu = z[c];
+                }
+                double den = 0.0;
+                for (int64_t c = 0; c <= r; ++c) den += exp(z[c] - mu);
+                for (int64_t c = 0; c <= r; ++c) {
+                    double p = exp(z[c] - mu) / den;
+                    for (int64_t d = 0; d < D; ++d) o[d] += p * load_elem(v, head + c * D + d, dtype);
+                }
+            }
+        }
+    }
+    free(z);
+    return OK;
+}

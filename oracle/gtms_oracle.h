@@ -60,6 +60,14 @@ int gtms_oracle_masked_backward_f64(const void* y, const void* dy, double* dx,
                                     int64_t mask_sr, const int32_t* seq_lens, int64_t B,
                                     int64_t M, int64_t S, float scale, int dtype);
 
+/* Attention with the grouped tril mask (self-attention article, sections 1-2: scores,
+ * softmax, weighted sum of values): Q, K, V [B, M, S, D] in the element type; for query row
+ * r < L_b, out[r] = sum_{c <= r} softmax_c(scale * Q[r].K[c]) V[c]; rows r >= L_b are zero.
+ * out receives B*M*S*D fp64 values. */
+int gtms_oracle_attention_f64(const void* q, const void* k, const void* v, double* out,
+                              const int32_t* seq_lens, int64_t B, int64_t M, int64_t S,
+                              int64_t D, float scale, int dtype);
+
 /* The element codec, exported so that it can be pinned on its own. */
 double gtms_oracle_decode(uint32_t bits, int dtype);
 uint32_t gtms_oracle_encode(double v, int dtype);

@@ -8,7 +8,8 @@ Sources of the facts:
   * page "Fused grouped tril mask softmax" (github aoxy/Attention-Mask-Optimization README):
     the masks and the output printed for its worked example (``golden/``), and the
     operator-behaviour listing (masked_fill with the most negative value, then softmax);
-  * page "ops(8) self-attention CUDA (下)", section 2.1: the softmax derivative;
+  * page "ops(8) self-attention CUDA (下)", section 2.1: the softmax derivative; sections 1-2:
+    attention as scores, row softmax and weighted sum of values;
   * page "优化ScaledMaskSoftmax算子", sections 2.1, 4.1 and 6: the mask variants (minus
     infinity before the softmax, zero rows when every element is masked, masks built with
     tril, broadcast per-task masks, per-sample length masks);
@@ -642,9 +643,68 @@ def pin_variant_backward(orc):
         assert np.array_equal(fn(yp, gp), dx)
 
 
+# ------------------------------------------------------------------------------ attention
+# The self-attention article ("ops(8) self-attention CUDA") computes scores Q K^T, a softmax
+# per score row and the weighted sum P V; with this operation's mask a query row r < L keeps
+# the keys c <= r and a row r >= L is zero.
+
+def pin_attention(orc):
+    """(i) Equal to torch's float64 scaled_dot_product_attention with is_causal=True on the
+    rows below each length, zero on the others, for several head sizes and lengths.
+    (ii) Closed forms: row 0 is V[0]; keys all zero give the running mean of V; values all
+    equal to one vector u give u. (iii) The values in padded query rows and in keys or values
+    past the length never matter."""
+    import torch
+    rng = np.random.default_rng(41)
+    for D in (1, 8, 64):
+        S = 9
+        lens = [9, 5, 1, 0, 12]
+        B, M = len(lens), 2
+        q, k, v = (rng.uniform(-2, 2, size=(B, M, S, D)).astype(np.float32) for _ in range(3))
+        scale = 0.7
+        o = orc.attention_f64(q, k, v, lens, scale, F32)
+        t = [torch.as_tensor(a.astype(np.float64)) for a in (q, k, v)]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            *t, is_causal=True, scale=float(np.float32(scale))).numpy()
+        for b, L in enumerate(lens):
+            Lc = min(max(L, 0), S)
+            assert np.allclose(o[b, :, :Lc], ref[b, :, :Lc], rtol=0, atol=1e-14), (D, L)
+            assert np.all(o[b, :, Lc:] == 0.0)
+            if Lc:
+                assert np.allclose(o[b, :, 0], v[b, :, 0], rtol=0, atol=1e-15)
+        # poison: queries of padded rows, keys and values past each length
+        qp, kp, vp = q.copy(), k.copy(), v.copy()
+        for b, L in enumerate(lens):
+            Lc = min(max(L, 0), S)
+            qp[b, :, Lc:] = np.nan
+            kp[b, :, Lc:] = np.inf
+            vp[b, :, Lc:] = np.nan
+        assert np.array_equal(orc.attention_f64(qp, kp, vp, lens, scale, F32), o)
+    S, D = 7, 4
+    v = rng.normal(size=(1, 1, S, D)).astype(np.float32)
+    q = rng.normal(size=(1, 1, S, D)).astype(np.float32)
+    o = orc.attention_f64(q, np.zeros_like(q), v, [S], 1.0, F32)
+    for r in range(S):
+        assert np.allclose(o[0, 0, r], v[0, 0, :r + 1].astype(np.float64).mean(0), rtol=0, atol=1e-15)
+    u = rng.normal(size=(D,)).astype(np.float32)
+    vv = np.broadcast_to(u, (1, 1, S, D)).copy()
+    o = orc.attention_f64(q, rng.normal(size=q.shape).astype(np.float32), vv, [S], 1.3, F32)
+    assert np.allclose(o[0, 0], np.broadcast_to(u.astype(np.float64), (S, D)), rtol=0, atol=1e-14)
+    # 16-bit inputs are decoded exactly: the same values in binary32 give the same result
+    q16 = rng.normal(size=(1, 2, S, 8)).astype(np.float16)
+    k16 = rng.normal(size=(1, 2, S, 8)).astype(np.float16)
+    v16 = rng.normal(size=(1, 2, S, 8)).astype(np.float16)
+    a = orc.attention_f64(q16.view(np.uint16), k16.view(np.uint16), v16.view(np.uint16), [S],
+                          0.5, F16)
+    b = orc.attention_f64(q16.astype(np.float32), k16.astype(np.float32),
+                          v16.astype(np.float32), [S], 0.5, F32)
+    assert np.array_equal(a, b)
+
+
 ALL_PINS = [
     pin_printed_masks, pin_printed_output, pin_row0, pin_row_sums, pin_exact_zeros,
     pin_brute_force, pin_closed_forms, pin_shift_and_scale, pin_masked_poison,
     pin_length_edges, pin_codec, pin_rounded_outputs, pin_rows_api, pin_backward,
     pin_band_brute_force, pin_band_closed_forms, pin_masked_brute_force, pin_variant_backward,
+    pin_attention,
 ]
