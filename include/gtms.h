@@ -190,6 +190,26 @@ int gtms_backward_masked(const void* y, const void* dy, void* dx, const uint8_t*
                          const int32_t* seq_lens, int64_t B, int64_t M, int64_t S, float scale,
                          int dtype, int path, unsigned flags, void* stream);
 
+/*
+ * Attention with the grouped tril mask, fused (the self-attention article, "ops(8)
+ * self-attention CUDA": scores, row softmax, weighted sum of values; here the softmax is
+ * the grouped tril mask softmax of gtms_forward):
+ *   for query row r < L_b:  out[r] = sum_{c <= r} softmax_c(scale * q[r] . k[c]) v[c]
+ *   for query row r >= L_b: out[r] = 0
+ * q, k, v, out  [B, M, S, D] elements of `dtype`, row-major, contiguous: M heads per batch
+ *               entry, S positions, head size D. out may overlap none of q, k, v.
+ * seq_lens      B int32 valid lengths (clamped to [0, S] on the device).
+ * dtype         GTMS_F16 or GTMS_BF16 (GTMS_ERR_DTYPE otherwise); the scores, the softmax
+ *               and the sums are fp32; the probabilities are rounded to `dtype` before the
+ *               product with v (matrix-core operands); out is rounded to nearest-even.
+ * D             64 or 128 (GTMS_ERR_PATH otherwise).
+ * All pointers 16-byte aligned (GTMS_ERR_ALIGN). One head (S * D elements) must be below
+ * 2^30 elements. The S x S scores are never written to memory.
+ */
+int gtms_attention_forward(const void* q, const void* k, const void* v, void* out,
+                           const int32_t* seq_lens, int64_t B, int64_t M, int64_t S, int64_t D,
+                           float scale, int dtype, void* stream);
+
 /* A static, human-readable description of a status code. */
 const char* gtms_status_string(int status);
 

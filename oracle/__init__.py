@@ -95,6 +95,9 @@ class Oracle:
         lib.gtms_oracle_masked_backward_f64.restype = i32
         lib.gtms_oracle_attention_f64.argtypes = [p, p, p, p, p, i64, i64, i64, i64, f32, i32]
         lib.gtms_oracle_attention_f64.restype = i32
+        lib.gtms_oracle_attention_row_f64.argtypes = [p, p, p, p, i64, ctypes.c_int32, i64, i64,
+                                                      f32, i32]
+        lib.gtms_oracle_attention_row_f64.restype = i32
         lib.gtms_oracle_decode.argtypes = [ctypes.c_uint32, i32]
         lib.gtms_oracle_decode.restype = ctypes.c_double
         lib.gtms_oracle_encode.argtypes = [ctypes.c_double, i32]
@@ -233,6 +236,18 @@ class Oracle:
                      "gtms_oracle_attention_f64")
         return o
 
+    def attention_row_f64(self, q_head: np.ndarray, k_head: np.ndarray, v_head: np.ndarray,
+                          r: int, seq_len: int, scale: float, dtype: int = F32) -> np.ndarray:
+        """fp64 attention output of query row r of one head ([S, D] raw storage each)."""
+        q, k, v = _check(q_head, dtype), _check(k_head, dtype), _check(v_head, dtype)
+        S, D = q.shape
+        o = np.empty(D, dtype=np.float64)
+        self._status(self.lib.gtms_oracle_attention_row_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                                            int(r), int(seq_len), S, D, scale,
+                                                            dtype),
+                     "gtms_oracle_attention_row_f64")
+        return o
+
     def decode(self, bits: int, dtype: int) -> float:
         return self.lib.gtms_oracle_decode(int(bits), dtype)
 
@@ -303,3 +318,7 @@ def masked_backward_f64(*a, **k):
 
 def attention_f64(*a, **k):
     return default().attention_f64(*a, **k)
+
+
+def attention_row_f64(*a, **k):
+    return default().attention_row_f64(*a, **k)

@@ -462,6 +462,29 @@ int gtms_oracle_masked_backward_f64(const void* y, const void* dy, double* dx,
  * while a query row r >= L is all zeros (a padded row of the softmax gives P = 0).
  * Q, K, V and O are [B, M, S, D], row-major, in the element type; out receives fp64.
  * ------------------------------------------------------------------------------------ */
+/* One query row r of a head: q, k and v point at the head's first element ([S, D]); o
+ * receives D values; z is scratch for r + 1 scores. */
+static void attention_row(const void* q, const void* k, const void* v, int64_t r, int64_t L,
+                          int64_t D, double scale, int dtype, double* z, double* o) {
+    for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+    if (r >= L) return;
+    /* scores of the kept keys c = 0..r and their maximum */
+    double mu = -INFINITY;
+    for (int64_t c = 0; c <= r; ++c) {
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d)
+            dot += load_elem(q, r * D + d, dtype) * load_elem(k, c * D + d, dtype);
+        z[c] = scale * dot;
+        if (z[c] > mu) mu = z[c];
+    }
+    double den = 0.0;
+    for (int64_t c = 0; c <= r; ++c) den += exp(z[c] - mu);
+    for (int64_t c = 0; c <= r; ++c) {
+        double p = exp(z[c] - mu) / den;
+        for (int64_t d = 0; d < D; ++d) o[d] += p * load_elem(v, c * D + d, dtype);
+    }
+}
+
 int gtms_oracle_attention_f64(const void* q, const void* k, const void* v, double* out,
                               const int32_t* seq_lens, int64_t B, int64_t M, int64_t S,
                               int64_t D, float scale, int dtype) {
@@ -480,29 +503,27 @@ int gtms_oracle_attention_f64(const void* q, const void* k, const void* v, doubl
         int64_t L = valid_length(seq_lens[b], S);
         for (int64_t m = 0; m < M; ++m) {
             int64_t head = (b * M + m) * S * D;  /* first element of this head's [S, D] */
-            for (int64_t r = 0; r < S; ++r) {
-                double* o = out + head + r * D;
-                for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
-                if (r >= L) continue;
-                /* scores of the kept keys c = 0..r and their maximum */
-                double mu = -INFINITY;
-                for (int64_t c = 0; c <= r; ++c) {
-                    double dot = 0.0;
-                    for (int64_t d = 0; d < D; ++d)
-                        dot += load_elem(q, head + r * D + d, dtype) *
-                               load_elem(k, head + c * D + d, dtype);
-                    z[c] = (double)scale * dot;
-                    if (z[c] > mu) mu = z[c];
-                }
-                double den = 0.0;
-                for (int64_t c = 0; c <= r; ++c) den += exp(z[c] - mu);
-                for (int64_t c = 0; c <= r; ++c) {
-                    double p = exp(z[c] - mu) / den;
-                    for (int64_t d = 0; d < D; ++d) o[d] += p * load_elem(v, head + c * D + d, dtype);
-                }
-            }
+            for (int64_t r = 0; r < S; ++r)
+                attention_row((const unsigned char*)q + head * bytes,
+                              (const unsigned char*)k + head * bytes,
+                              (const unsigned char*)v + head * bytes, r, L, D, (double)scale,
+                              dtype, z, out + head + r * D);
         }
     }
+    free(z);
+    return OK;
+}
+
+int gtms_oracle_attention_row_f64(const void* q, const void* k, const void* v, double* out,
+                                  int64_t r, int32_t seq_len, int64_t S, int64_t D,
+                                  float scale, int dtype) {
+    int ebits, pbits, bytes;
+    if (!format_of(dtype, &ebits, &pbits, &bytes)) return ERR_DTYPE;
+    if (S < 0 || D < 0 || r < 0 || r >= S) return ERR_ARG;
+    if (!q || !k || !v || !out) return ERR_ARG;
+    double* z = (double*)malloc((size_t)(r + 1) * sizeof(double));
+    if (!z) return ERR_ARG;
+    attention_row(q, k, v, r, valid_length(seq_len, S), D, (double)scale, dtype, z, out);
     free(z);
     return OK;
 }

@@ -68,6 +68,12 @@ int gtms_oracle_attention_f64(const void* q, const void* k, const void* v, doubl
                               const int32_t* seq_lens, int64_t B, int64_t M, int64_t S,
                               int64_t D, float scale, int dtype);
 
+/* One query row r of one head: q, k, v point at the head's [S, D] elements; out receives
+ * the D fp64 values of row r for a batch of raw valid length seq_len. */
+int gtms_oracle_attention_row_f64(const void* q, const void* k, const void* v, double* out,
+                                  int64_t r, int32_t seq_len, int64_t S, int64_t D,
+                                  float scale, int dtype);
+
 /* The element codec, exported so that it can be pinned on its own. */
 double gtms_oracle_decode(uint32_t bits, int dtype);
 uint32_t gtms_oracle_encode(double v, int dtype);

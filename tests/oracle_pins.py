@@ -680,6 +680,10 @@ def pin_attention(orc):
             kp[b, :, Lc:] = np.inf
             vp[b, :, Lc:] = np.nan
         assert np.array_equal(orc.attention_f64(qp, kp, vp, lens, scale, F32), o)
+        # the one-row entry point gives the same bits as the full one
+        for b, m, r in ((0, 1, 8), (1, 0, 3), (1, 0, 7), (2, 1, 0), (3, 0, 4)):
+            row = orc.attention_row_f64(q[b, m], k[b, m], v[b, m], r, lens[b], scale, F32)
+            assert np.array_equal(row, o[b, m, r])
     S, D = 7, 4
     v = rng.normal(size=(1, 1, S, D)).astype(np.float32)
     q = rng.normal(size=(1, 1, S, D)).astype(np.float32)

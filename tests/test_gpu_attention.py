@@ -1,0 +1,145 @@
+"""GPU parity of the fused attention with the grouped tril mask against the CPU oracle.
+
+The kernel computes, per query row r < L_b, sum_{c <= r} softmax(scale * q_r . k_c) v_c and
+writes zeros for rows r >= L_b (the self-attention article's three steps with this
+operation's softmax). Rows at or past the length must be +0.0 bit for bit. Kept rows must
+satisfy, element by element, a bound derived from the arithmetic: the scores, exponentials
+and sums are fp32 (relative errors of a few 2^-24), and two roundings into the element type
+dominate, that of each probability before the product with v (relative u, so at most
+u * sum_c p_c |v_c| <= u * max_c |v_c| in the row) and that of the output (u * |o|):
+    |o_gpu - o_ref| <= u * (max_{c <= r} |v_c| + |o_ref|) + 1e-5 * max_{c <= r} |v_c|
+with u = 2^-8 for bfloat16 and 2^-11 for binary16 (half an ulp of a 9- or 12-bit
+significand).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gtms_check import bits, to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("GPU tests need a visible GPU", allow_module_level=True)
+
+import variable_length_causal_amd as g  # noqa: E402
+
+DTYPES = [workloads.F16, workloads.BF16]
+DNAME = {workloads.F16: "f16", workloads.BF16: "bf16"}
+U = {workloads.F16: 2.0 ** -11, workloads.BF16: 2.0 ** -8}
+
+
+def prefix_vmax(v_head_f64):
+    """[S] running max over rows c <= r of max_d |v[c, d]| for one head [S, D]."""
+    return np.maximum.accumulate(np.max(np.abs(v_head_f64), axis=1))
+
+
+def check_rows(o_st, ref, vmax_rows, lens_rows, rows_r, S, dtype, tag):
+    """o_st, ref: [n, D]; row i has index rows_r[i], length lens_rows[i] and
+    vmax_rows[i] = max over its kept keys of |v|."""
+    got = to_f64(o_st, dtype)
+    ob = bits(o_st)
+    for i, (L, r) in enumerate(zip(lens_rows, rows_r)):
+        Lc = min(max(int(L), 0), S)
+        if r >= Lc:
+            assert not ob[i].any(), f"{tag}: row {r} >= L={L} is not zero"
+            continue
+        vmax = float(vmax_rows[i])
+        bound = U[dtype] * (vmax + np.abs(ref[i])) + 1e-5 * vmax
+        err = np.abs(got[i] - ref[i])
+        assert np.all(err <= bound), f"{tag}: row {r} L={L} excess {float(np.max(err - bound)):.3g}"
+
+
+def run_case(B, M, S, D, dtype, lens, scale, seed):
+    shape = (B, M, S, D)
+    q, k, v = (workloads.scores_cpu(shape, dtype, 1.0, seed + i) for i in range(3))
+    qs, ks, vs = (workloads.to_storage(t) for t in (q, k, v))
+    ref = oracle.attention_f64(qs, ks, vs, lens, scale, dtype)
+    print(f"attention B={B} M={M} S={S} D={D} {DNAME[dtype]} lens={list(lens)}", flush=True)
+    o = g.attention(q.cuda(), k.cuda(), v.cuda(), torch.as_tensor(np.asarray(lens, np.int32)).cuda(),
+                    scale)
+    torch.cuda.synchronize()
+    o_st = workloads.to_storage(o.cpu())
+    vf = to_f64(vs, dtype)
+    for b in range(B):
+        for m in range(M):
+            check_rows(o_st[b, m], ref[b, m], prefix_vmax(vf[b, m]), [lens[b]] * S,
+                       range(S), S, dtype, f"B={B} M={M} S={S} D={D} {DNAME[dtype]} b={b} m={m}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DNAME[d])
+@pytest.mark.parametrize("D", [64, 128])
+def test_attention_shapes(dtype, D):
+    for S in (1, 5, 31, 32, 33, 127, 128, 129, 300):
+        lens = [S, max(1, S // 3), 0, S + 7]
+        run_case(len(lens), 2, S, D, dtype, lens, 1.0 / np.sqrt(D), seed=10 * S + D)
+
+
+def test_attention_scales_and_long_rows():
+    run_case(2, 2, 1000, 64, workloads.BF16, [1000, 611], 0.3, seed=5)
+    run_case(1, 1, 700, 128, workloads.F16, [700], 0.05, seed=6)
+    run_case(2, 1, 200, 64, workloads.F16, [200, 150], 2.0, seed=7)
+
+
+def test_attention_ignores_padding():
+    """Queries of padded rows and keys/values at or past the length change no bit."""
+    B, M, S, D = 3, 2, 260, 64
+    lens = [260, 100, 0]
+    for dtype in DTYPES:
+        q, k, v = (workloads.scores_cpu((B, M, S, D), dtype, 1.0, 50 + i).cuda() for i in range(3))
+        sl = torch.as_tensor(np.asarray(lens, np.int32)).cuda()
+        clean = g.attention(q, k, v, sl)
+        qp, kp, vp = q.clone(), k.clone(), v.clone()
+        for b, L in enumerate(lens):
+            qp[b, :, L:] = float("nan")
+            kp[b, :, L:] = float("inf")
+            vp[b, :, L:] = float("nan")
+        dirty = g.attention(qp, kp, vp, sl)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(workloads.to_storage(clean.cpu())),
+                              bits(workloads.to_storage(dirty.cpu())))
+
+
+def test_attention_rejects_bad_arguments():
+    q = torch.zeros(1, 1, 64, 64, dtype=torch.float16, device="cuda")
+    sl = torch.ones(1, dtype=torch.int32, device="cuda")
+    with pytest.raises(RuntimeError):   # head size 32 is not served
+        g.attention(torch.zeros(1, 1, 64, 32, dtype=torch.float16, device="cuda"),
+                    torch.zeros(1, 1, 64, 32, dtype=torch.float16, device="cuda"),
+                    torch.zeros(1, 1, 64, 32, dtype=torch.float16, device="cuda"), sl)
+    with pytest.raises(RuntimeError, match="element type"):  # no binary32 path
+        g.attention(q.float(), q.float(), q.float(), sl)
+    with pytest.raises(RuntimeError):   # out over q
+        g.attention(q, q.clone(), q.clone(), sl, out=q)
+
+
+@pytest.mark.parametrize("name", sorted(workloads.ATTN_WORKLOADS))
+def test_attention_full_workload_sampled(name):
+    """The benchmark's shapes at full size: sampled rows against the oracle's one-row
+    entry point, plus every padded row zero and every output finite."""
+    w = workloads.ATTN_WORKLOADS[name]
+    lens = workloads.seq_lens(w)
+    q, k, v = (workloads.scores_device(w.shape, w.dtype, 1.0, w.x_seed + i, "cuda")
+               for i in range(3))
+    o = g.attention(q, k, v, torch.as_tensor(lens).cuda(), w.scale)
+    torch.cuda.synchronize()
+    for b, L in enumerate(lens):
+        assert not torch.any(o[b, :, int(L):] != 0).item(), f"padded rows of batch {b}"
+        assert torch.isfinite(o[b, :, :int(L)]).all().item()
+    rng = np.random.default_rng(9)
+    picks = [(int(rng.integers(w.B)), int(rng.integers(w.M)), None) for _ in range(24)]
+    rows = []
+    for b, m, _ in picks:
+        L = int(lens[b])
+        for r in (int(rng.integers(L)), L - 1, 0):
+            rows.append((b, m, r))
+    for b, m, r in rows:
+        qs, ks, vs = (workloads.to_storage(t[b, m].cpu()) for t in (q, k, v))
+        ref = oracle.attention_row_f64(qs, ks, vs, r, int(lens[b]), w.scale, w.dtype)
+        ost = workloads.to_storage(o[b, m, r:r + 1].cpu())
+        vmax = prefix_vmax(to_f64(vs, w.dtype))[r]
+        check_rows(ost, ref[None], [vmax], [lens[b]], [r], w.S, w.dtype, f"{name} b={b} m={m}")

@@ -49,14 +49,14 @@ MUTATIONS = {
                                      "        double z = load_elem(x, c, dtype);\n        if (z > mu) mu = z;\n        ++nkept;\n    }\n    if (nkept == 0) {\n        for"),
     "variant_backward_sign": ("(load_elem(g, c, dtype) - dot)", "(load_elem(g, c, dtype) + dot)"),
     # attention
-    "attention_diagonal_dropped": ("for (int64_t c = 0; c <= r; ++c) {\n                    double dot = 0.0;",
-                                   "for (int64_t c = 0; c < r; ++c) {\n                    double dot = 0.0;"),
-    "attention_scale_dropped": ("z[c] = (double)scale * dot;", "z[c] = dot;"),
-    "attention_key_transposed": ("load_elem(k, head + c * D + d, dtype);",
-                                 "load_elem(k, head + d * S + c, dtype);"),
-    "attention_padded_rows_kept": ("if (r >= L) continue;", "if (r >= S) continue;"),
-    "attention_value_row_of_query": ("o[d] += p * load_elem(v, head + c * D + d, dtype);",
-                                     "o[d] += p * load_elem(v, head + r * D + d, dtype);"),
+    "attention_diagonal_dropped": ("for (int64_t c = 0; c <= r; ++c) {\n        double dot = 0.0;",
+                                   "for (int64_t c = 0; c < r; ++c) {\n        double dot = 0.0;"),
+    "attention_scale_dropped": ("z[c] = scale * dot;", "z[c] = dot;"),
+    "attention_key_transposed": ("load_elem(k, c * D + d, dtype);",
+                                 "load_elem(k, d * (r + 1) + c, dtype);"),
+    "attention_padded_rows_kept": ("    if (r >= L) return;\n    /* scores", "    if (r >= L + 1) return;\n    /* scores"),
+    "attention_value_row_of_query": ("o[d] += p * load_elem(v, c * D + d, dtype);",
+                                     "o[d] += p * load_elem(v, r * D + d, dtype);"),
     "variant_backward_dot_unmasked": ("if (keep[c]) dot += load_elem(g, c, dtype) * load_elem(y, c, dtype);",
                                       "dot += load_elem(g, c, dtype) * load_elem(y, c, dtype);"),
 }

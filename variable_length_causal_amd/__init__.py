@@ -9,6 +9,7 @@ on the caller's current torch stream. Torch provides device memory and streams.
     y = forward_band(x, seq_lens, lo, hi, scale)   # kept: lo <= c - r <= hi
     y = forward_masked(x, mask, seq_lens, scale)   # kept: mask != 0 ([B|1, M|1, S|1, S])
     dx = backward_band(...), backward_masked(...)  # their gradients
+    o = attention(q, k, v, seq_lens, scale)        # fused: q, k, v [B, M, S, D] f16/bf16
 
 There is no fallback: if the library is missing or cannot load, every call raises.
 """
@@ -61,6 +62,8 @@ def _load():
     lib.gtms_backward_masked.argtypes = [p, p, p, p, i64, i64, i64, p, i64, i64, i64, f32, i32,
                                          i32, u32, p]
     lib.gtms_backward_masked.restype = i32
+    lib.gtms_attention_forward.argtypes = [p, p, p, p, p, i64, i64, i64, i64, f32, i32, p]
+    lib.gtms_attention_forward.restype = i32
     lib.gtms_status_string.argtypes = [i32]
     lib.gtms_status_string.restype = ctypes.c_char_p
     lib.gtms_version.argtypes = []
@@ -320,4 +323,33 @@ def backward_masked(y, dy, mask, seq_lens=None, scale: float = 1.0, out=None,
                                     sb, sm, sr, _lens_ptr(seq_lens, y), B, M, S, float(scale),
                                     _dtype_code(y), PATHS[path], int(flags), _stream_of(y))
     _raise(st, "gtms_backward_masked")
+    return out
+
+
+def attention(q, k, v, seq_lens, scale: float | None = None, out=None):
+    """Fused attention with the grouped tril mask: for query row r < L_b,
+    out[r] = sum_{c <= r} softmax_c(scale * q[r].k[c]) v[c]; rows r >= L_b are zero.
+    q, k, v: [B, M, S, D] float16 or bfloat16 GPU tensors, D = 64 or 128. The default scale
+    is 1 / sqrt(D)."""
+    import math
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, M, S, D] GPU tensor")
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k and v must match in shape, dtype and device")
+    _check_lens(seq_lens, q)
+    B, M, S, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() \
+            or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor of q's shape, dtype and device")
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    L = _load()
+    with _on_device(q):
+        st = L.gtms_attention_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                      seq_lens.data_ptr(), B, M, S, D, sc, _dtype_code(q),
+                                      _stream_of(q))
+    _raise(st, "gtms_attention_forward")
     return out

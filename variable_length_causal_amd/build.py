@@ -1,8 +1,9 @@
 """Build libgtms.so (the HIP kernels and the C ABI) for gfx950 with hipcc, in-tree.
 
 The kernel launchers are compiled once per operation (forward, backward) and mask kind
-(tril, band, explicit mask) from launch_kind.hip, in parallel, next to the host logic in
-gtms_api.hip; the objects are then linked into one shared library.
+(tril, band, explicit mask) from launch_kind.hip, in parallel with the fused attention
+launcher (launch_attention.hip) and the host logic (gtms_api.hip); the objects are then
+linked into one shared library.
 """
 from __future__ import annotations
 
@@ -26,7 +27,7 @@ HIPCC_FLAGS = [
 ]
 
 # (source, extra defines) of every object in the library
-UNITS = [("gtms_api.hip", [])] + [
+UNITS = [("gtms_api.hip", []), ("launch_attention.hip", [])] + [
     ("launch_kind.hip", [f"-DGTMS_OP={op}", f"-DGTMS_MK={mk}"])
     for op in (0, 1) for mk in (0, 1, 2)
 ]

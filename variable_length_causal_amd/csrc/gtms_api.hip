@@ -192,6 +192,46 @@ int run_impl(const void* x, const void* g, void* out, const int32_t* seq_lens, i
     return e == hipSuccess ? GTMS_OK : GTMS_ERR_HIP;
 }
 
+int attention_impl(const void* q, const void* k, const void* v, void* out,
+                   const int32_t* seq_lens, int64_t B, int64_t M, int64_t S, int64_t D,
+                   float scale, int dtype, void* stream) {
+    if (dtype != GTMS_F16 && dtype != GTMS_BF16) return GTMS_ERR_DTYPE;
+    if (B < 0 || M < 0 || S < 0 || D < 0 || S > GTMS_MAX_S || M > INT32_MAX)
+        return GTMS_ERR_INVALID_ARG;
+    int64_t planes = 0, bytes = 0;
+    if (__builtin_mul_overflow(B, M, &planes) || __builtin_mul_overflow(planes, S * D * 2, &bytes))
+        return GTMS_ERR_INVALID_ARG;
+    // one head's byte offsets, up to the last query tile's end, stay below 2^31
+    if ((S + kAttnRows) * D * 2 >= (int64_t(1) << 31)) return GTMS_ERR_INVALID_ARG;
+    if (bytes == 0) return GTMS_OK;
+    if (D != 64 && D != 128) return GTMS_ERR_PATH;
+    if (!q || !k || !v || !out || !seq_lens) return GTMS_ERR_INVALID_ARG;
+    if ((uintptr_t)q % 16 || (uintptr_t)k % 16 || (uintptr_t)v % 16 || (uintptr_t)out % 16 ||
+        (uintptr_t)seq_lens % 4)
+        return GTMS_ERR_ALIGN;
+    // the output may overlap no input: blocks read keys and values of rows other blocks write
+    for (const void* in : {q, k, v}) {
+        const uintptr_t x = (uintptr_t)in, y = (uintptr_t)out;
+        if (x < y + (uintptr_t)bytes && y < x + (uintptr_t)bytes) return GTMS_ERR_INVALID_ARG;
+    }
+    const int64_t tiles = (S + kAttnRows - 1) / kAttnRows;
+    if (planes > (int64_t)UINT32_MAX || planes * tiles > (int64_t)INT32_MAX)
+        return GTMS_ERR_INVALID_ARG;
+    AttnArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = out;
+    a.seq_lens = seq_lens;
+    a.n_planes = (uint32_t)planes;
+    a.M = (uint32_t)M;
+    a.S = (int)S;
+    a.n_tiles = (int)tiles;
+    a.k2 = (float)((double)scale * 1.4426950408889634074);
+    const hipError_t e = launch_attention(dtype, (int)D, a, (hipStream_t)stream);
+    return e == hipSuccess ? GTMS_OK : GTMS_ERR_HIP;
+}
+
 MaskSpec band(int64_t lo, int64_t hi) {
     MaskSpec m;
     m.kind = MK_BAND;
@@ -286,6 +326,12 @@ int gtms_backward_masked(const void* y, const void* dy, void* dx, const uint8_t*
     return gtms::run_impl<gtms::OP_BWD>(
         y, dy, dx, seq_lens, B, M, S, scale, dtype, path, flags, stream,
         gtms::explicit_mask(mask, mask_stride_b, mask_stride_m, mask_stride_r));
+}
+
+int gtms_attention_forward(const void* q, const void* k, const void* v, void* out,
+                           const int32_t* seq_lens, int64_t B, int64_t M, int64_t S, int64_t D,
+                           float scale, int dtype, void* stream) {
+    return gtms::attention_impl(q, k, v, out, seq_lens, B, M, S, D, scale, dtype, stream);
 }
 
 const char* gtms_status_string(int status) {

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "attention_kernels.h"
 #include "forward_kernels.h"
 
 namespace gtms {
@@ -37,5 +38,9 @@ extern template hipError_t launch_kind<OP_FWD, MK_MASK>(int, const Plan&, const 
 extern template hipError_t launch_kind<OP_BWD, MK_TRIL>(int, const Plan&, const FwdArgs&, hipStream_t);
 extern template hipError_t launch_kind<OP_BWD, MK_BAND>(int, const Plan&, const FwdArgs&, hipStream_t);
 extern template hipError_t launch_kind<OP_BWD, MK_MASK>(int, const Plan&, const FwdArgs&, hipStream_t);
+
+// Launches the fused attention kernel for element type `dtype` (GTMS_F16 or GTMS_BF16) and
+// head size D (64 or 128).
+hipError_t launch_attention(int dtype, int D, const AttnArgs& a, hipStream_t st);
 
 }  // namespace gtms

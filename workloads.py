@@ -66,6 +66,47 @@ WORKLOADS = {
 }
 
 
+@dataclass(frozen=True)
+class AttnWorkload:
+    """Inputs of the fused attention: q, k, v [B, M, S, D] normal, per-batch lengths."""
+    name: str
+    B: int
+    M: int
+    S: int
+    D: int
+    dtype: int
+    len_lo: int = 0
+    len_hi: int = 0
+    fixed_lens: tuple = field(default=())
+    x_seed: int = 0
+    len_seed: int = 0
+
+    @property
+    def shape(self):
+        return (self.B, self.M, self.S, self.D)
+
+    @property
+    def esize(self) -> int:
+        return ESIZE[self.dtype]
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.D))
+
+
+ATTN_WORKLOADS = {
+    # batch 32 at sequence 4096 with head size 64 (ScaledMaskSoftmax article, test
+    # conditions of its timing table) and 8 heads (the H of the README's configurations);
+    # lengths as in scaled_f16_32x1x4096
+    "attn_bf16_32x8x4096_d64": AttnWorkload("attn_bf16_32x8x4096_d64", 32, 8, 4096, 64, BF16,
+                                            512, 4096, x_seed=1104, len_seed=2004),
+    # the README's B = 3, M = 64, S = 1000, read as 64 heads of size 64; lengths as in
+    # readme_f32_3x64x1000
+    "attn_f16_3x64x1000_d64": AttnWorkload("attn_f16_3x64x1000_d64", 3, 64, 1000, 64, F16,
+                                           1, 1000, x_seed=1102, len_seed=2002),
+}
+
+
 def seq_lens(w: Workload, seed: int | None = None) -> np.ndarray:
     """int32[B] valid lengths for a workload."""
     if w.fixed_lens:
