@@ -38,11 +38,13 @@ import numpy as np  # noqa: E402
 import workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix-core peak, published
 METRIC = "ms and effective HBM GB/s (% of peak) for [B,M,S,S] masked softmax"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "variable_length_causal_amd", "csrc", f)
                   for f in ("device_common.h", "forward_kernels.h", "backward_kernels.h",
-                            "gtms_api.hip", "launch.h", "launch_kind.hip")]
+                            "gtms_api.hip", "launch.h", "launch_kind.hip",
+                            "attention_kernels.h", "launch_attention.hip")]
 
 
 def algorithmic_bytes(w: workloads.Workload, lens, op: str = "forward") -> int:
@@ -71,6 +73,73 @@ def variant_bytes(w: workloads.Workload, lens, variant: str, lo: int, hi: int,
     reads *= w.M
     writes = w.B * w.M * S * S
     return w.esize * ((2 if op == "backward" else 1) * reads + writes) + mask_bytes
+
+
+def attention_flops(w: workloads.AttnWorkload, lens) -> int:
+    """Multiply-adds x 2 of the kept pairs (query r < L, key c <= r): D for q.k and D for
+    the weighted sum of v, per pair."""
+    pairs = sum(w.M * min(max(int(L), 0), w.S) * (min(max(int(L), 0), w.S) + 1) // 2
+                for L in lens)
+    return 4 * w.D * pairs
+
+
+def bench_attention(args):
+    import torch
+    import variable_length_causal_amd as g
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workloads.ATTN_WORKLOADS[args.workload]
+    lens = workloads.seq_lens(w)
+    sl = torch.as_tensor(lens).to(dev)
+    flops = attention_flops(w, lens)
+    nsets = 2
+    qkv = [[workloads.scores_device(w.shape, w.dtype, 1.0, w.x_seed + 3 * i + j, dev)
+            for j in range(3)] for i in range(nsets)]
+    outs = [torch.empty_like(qkv[0][0]) for _ in range(nsets)]
+    torch.cuda.synchronize()
+
+    def step(i):
+        q, k, v = qkv[i % nsets]
+        g.attention(q, k, v, sl, w.scale, out=outs[i % nsets])
+
+    for i in range(args.warmup):
+        step(i)
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    avg_kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    achieved = flops / (avg_kernel_ms * 1e-3) / 1e12
+    out = {
+        "metric": "TFLOP/s of the fused attention with the grouped tril mask",
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": workloads.DTYPE_NAMES[w.dtype],
+        "data": "synthetic (seeded normal q, k, v generated on the device, seeded lengths)",
+        "config": {"workload": w.name, "op": "attention", "B": w.B, "M": w.M, "S": w.S,
+                   "D": w.D, "seq_lens": [int(v) for v in lens], "scale": w.scale,
+                   "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": MFMA16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(f"{w.name}:attention")},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
 
 
 def kernel_sources_hash() -> str:
@@ -132,10 +201,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="readme_f32_3x64x1000",
-                    choices=sorted(k for k in workloads.WORKLOADS if "example" not in k))
-    ap.add_argument("--op", default="forward", choices=["forward", "backward"],
-                    help="the forward (the headline) or its backward")
+    ap.add_argument("--workload", default=None,
+                    choices=sorted(k for k in workloads.WORKLOADS if "example" not in k) +
+                    sorted(workloads.ATTN_WORKLOADS))
+    ap.add_argument("--op", default="forward", choices=["forward", "backward", "attention"],
+                    help="the forward (the headline), its backward, or the fused attention")
     ap.add_argument("--variant", default="tril", choices=["tril", "band", "mask"],
                     help="the grouped tril mask (the headline), a band, or an explicit mask")
     ap.add_argument("--band", default="-511,0",
@@ -161,6 +231,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.op == "attention":
+        args.workload = args.workload or "attn_bf16_32x8x4096_d64"
+        if args.workload not in workloads.ATTN_WORKLOADS:
+            ap.error("--op attention takes an attention workload")
+        return bench_attention(args)
+    args.workload = args.workload or "readme_f32_3x64x1000"
+    if args.workload not in workloads.WORKLOADS:
+        ap.error(f"--op {args.op} takes a softmax workload")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = workloads.WORKLOADS[args.workload]

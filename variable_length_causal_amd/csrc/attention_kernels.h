@@ -11,10 +11,12 @@
 //
 // Work: one workgroup of 4 wavefronts per (plane, tile of 128 query rows); wavefront w owns
 // rows q0 + 32w .. q0 + 32w + 31, one row per lane pair (lanes l and l + 32 hold row l % 32).
-// Key blocks of 32 are staged in LDS (K row-major, V transposed) by the whole workgroup.
-// Per block each wavefront computes S^T = K Q^T with v_mfma_f32_32x32x16_{bf16,f16} (D/16
+// Key blocks of 64 are staged in LDS (K row-major, V transposed) by the whole workgroup; the
+// next block's K and V are loaded into registers while the current one computes. Per
+// 32-key tile each wavefront computes S^T = K Q^T with v_mfma_f32_32x32x16_{bf16,f16} (D/16
 // instructions; Q stays in registers as the B operand), so a lane holds 16 scores of ITS OWN
-// row: the row max and the rescaling are lane-local plus one exchange with lane l ^ 32. The
+// row: the row max and the rescaling are lane-local plus one exchange with lane l ^ 32.
+// Blocks wholly below the wavefront's diagonal and the length skip the mask. The
 // probabilities P are rounded to the element type and used, in the registers they were
 // computed in, as the B operand of O^T += V^T P^T (2 * D/32 instructions); the A operand
 // V^T is read from LDS in the key order the score layout implies (keys are a contraction
@@ -43,7 +45,8 @@ struct AttnArgs {
 };
 
 constexpr int kAttnRows = 128;  // query rows per workgroup (4 wavefronts x 32)
-constexpr int kAttnKeys = 32;   // keys per block
+// keys per block: 64 for head size 64, 32 for 128 (keeps two workgroups' registers per SIMD)
+template <int D> constexpr int kAttnKeys = D <= 64 ? 64 : 32;
 
 template <int DT> struct Mfma16;
 template <> struct Mfma16<DT_BF16> {
@@ -68,20 +71,31 @@ __device__ __forceinline__ float swap_halves(float v) {
 }
 
 template <int DT, int D>
-__global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : 2))) void attn_fwd(AttnArgs a) {
     using MF = Mfma16<DT>;
     using vec8 = typename MF::vec8;
     using elem_t = typename MF::elem_t;
     typedef elem_t vec4 __attribute__((ext_vector_type(4)));
+    typedef elem_t vec2 __attribute__((ext_vector_type(2)));
+    constexpr int BN = kAttnKeys<D>;       // keys per block
     constexpr int KP = D + 8;              // K row pitch in LDS (elements)
-    constexpr int VP = kAttnKeys + 4;      // V^T row pitch in LDS (elements)
+    constexpr int VP = BN + 8;             // V^T row pitch in LDS (elements, 16-byte rows)
     constexpr int NT = D / 32;             // 32-wide output tiles per row
-    __shared__ __attribute__((aligned(16))) elem_t k_lds[kAttnKeys * KP];
-    __shared__ __attribute__((aligned(16))) elem_t vt_lds[D * VP];
+    constexpr int CPR = D / 8;             // 16-byte chunks per K or V row
+    constexpr int KCH = BN * CPR / 256;    // K chunks per thread per block
+    constexpr int VCH = BN / 2 * CPR / 256;  // V key pairs (two chunks) per thread per block
+    static_assert(KCH >= 1 && VCH >= 1 && BN % 32 == 0, "block shape");
+    // two buffers: block i computes from buffer i % 2 while block i + 1 is written into the
+    // other one
+    __shared__ __attribute__((aligned(16))) elem_t k_lds[2][BN * KP];
+    __shared__ __attribute__((aligned(16))) elem_t vt_lds[2][D * VP];
 
-    // tiles with the most key blocks first: tile index descends with blockIdx
-    const uint32_t plane = blockIdx.x % a.n_planes;
-    const int qt = a.n_tiles - 1 - (int)(blockIdx.x / a.n_planes);
+    // Block order: all the tiles of one plane run on one XCD (its L2 then holds the
+    // plane's K and V once for all of them), the tiles with the most key blocks first.
+    const uint32_t nt = (uint32_t)a.n_tiles;
+    const uint32_t lb = xcd_grouped(blockIdx.x, gridDim.x, nt);
+    const uint32_t plane = lb / nt;
+    const int qt = (int)(nt - 1 - lb % nt);
     const int q0 = qt * kAttnRows;
     const int L = clamp_len(a.seq_lens[plane / a.M], a.S);
     const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6), g = lane >> 5;
@@ -92,98 +106,172 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
     // rows q0 .. q0+127 that lie at or past L are zeros (all of them when q0 >= L)
     {
         const int z0 = max(q0, L), z1 = min(q0 + kAttnRows, a.S);
-        for (int i = tid; i < (z1 - z0) * (D / 8); i += 256) {
-            const int r = z0 + i / (D / 8), c = (i % (D / 8)) * 8;
+        for (int i = tid; i < (z1 - z0) * CPR; i += 256) {
+            const int r = z0 + i / CPR, c = (i % CPR) * 8;
             __builtin_amdgcn_raw_buffer_store_b128(u32x4{0, 0, 0, 0}, out, (r * D + c) * 2, 0,
                                                    kPolicyStream);
         }
     }
     if (q0 >= L) return;
 
-    const int row = q0 + wave * 32 + (lane & 31);   // this lane's query row
-    const int kv_end = min(q0 + kAttnRows, L);       // keys the workgroup needs
-    const int wave_end = min(q0 + wave * 32 + 32, L);  // keys this wavefront needs
+    const int row = q0 + wave * 32 + (lane & 31);      // this lane's query row
+    const int row_lo = q0 + wave * 32;                 // the wavefront's first row
+    const int kv_end = min(q0 + kAttnRows, L);         // keys the workgroup needs
+    const int wave_end = min(row_lo + 32, L);          // keys this wavefront needs
 
     // Q^T as the B operand: lane l holds Q[row][16*kk + 8*g + j]
     const rsrc_t qin = make_rsrc((const char*)a.q + head * 2, head_bytes);
+    // A negative scale is applied as |scale| to -Q (a sign-bit flip, exact), so that the
+    // row max is always the max of the raw scores.
+    const uint32_t qsign = a.k2 < 0.0f ? 0x80008000u : 0u;
+    const float k2 = fabsf(a.k2);
     vec8 qf[D / 16];
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
         qf[kk] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(
-                                              qin, (row * D + 16 * kk + 8 * g) * 2, 0, 0));
+                                              qin, (row * D + 16 * kk + 8 * g) * 2, 0, 0) ^ qsign);
     // K and V of this head, keys < L only (the range check zero-fills keys past L, so the
     // masked probabilities meet finite values)
     const uint32_t kv_bytes = (uint32_t)((uint64_t)L * D * 2);
     const rsrc_t kin = make_rsrc((const char*)a.k + head * 2, kv_bytes);
     const rsrc_t vin = make_rsrc((const char*)a.v + head * 2, kv_bytes);
 
+    // the next block's K chunks and V key pairs, held in registers while a block computes
+    u32x4 kr[KCH], vr[VCH][2];
+    auto fetch = [&](int kb) {
+#pragma unroll
+        for (int n = 0; n < KCH; ++n) {
+            const int i = tid + 256 * n, key = i / CPR, c = (i % CPR) * 8;
+            kr[n] = __builtin_amdgcn_raw_buffer_load_b128(kin, ((kb + key) * D + c) * 2, 0, 0);
+        }
+#pragma unroll
+        for (int n = 0; n < VCH; ++n) {
+            const int i = tid + 256 * n, key = 2 * (i % (BN / 2)), c = (i / (BN / 2)) * 8;
+            vr[n][0] = __builtin_amdgcn_raw_buffer_load_b128(vin, ((kb + key) * D + c) * 2, 0, 0);
+            vr[n][1] = __builtin_amdgcn_raw_buffer_load_b128(vin, ((kb + key + 1) * D + c) * 2, 0, 0);
+        }
+    };
+    // K row-major; V transposed, two keys per 4-byte write: consecutive lanes take
+    // consecutive key pairs of one 8-column chunk, so that a write instruction covers whole
+    // LDS rows (no bank conflicts). Within each group of 16 keys the
+    // key 16h + 8a + 4b + i sits at column 16h + 8b + 4a + i, so that the 8 keys one lane
+    // needs for a product (b = its half of the wavefront, a = 0, 1) are one 16-byte read.
+    auto vcol = [](int key) { return (key & ~12) | ((key & 8) >> 1) | ((key & 4) << 1); };
+    auto stage = [&](int buf) {
+#pragma unroll
+        for (int n = 0; n < KCH; ++n) {
+            const int i = tid + 256 * n, key = i / CPR, c = (i % CPR) * 8;
+            *(u32x4*)&k_lds[buf][key * KP + c] = kr[n];
+        }
+#pragma unroll
+        for (int n = 0; n < VCH; ++n) {
+            const int i = tid + 256 * n, key = 2 * (i % (BN / 2)), c = (i / (BN / 2)) * 8;
+            const vec8 v0 = __builtin_bit_cast(vec8, vr[n][0]);
+            const vec8 v1 = __builtin_bit_cast(vec8, vr[n][1]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                *(vec2*)&vt_lds[buf][(c + j) * VP + vcol(key)] = vec2{v0[j], v1[j]};
+        }
+    };
+
     f32x16 acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
     float m_run = -INFINITY, l_part = 0.0f;
 
-    for (int kb = 0; kb < kv_end; kb += kAttnKeys) {
-        // stage the block: K row-major, V transposed (vt[d][key])
-        __syncthreads();  // the previous block's readers are done
-#pragma unroll
-        for (int i = tid; i < kAttnKeys * (D / 8); i += 256) {
-            const int key = i / (D / 8), c = (i % (D / 8)) * 8;
-            const int off = ((kb + key) * D + c) * 2;
-            const u32x4 kw = __builtin_amdgcn_raw_buffer_load_b128(kin, off, 0, 0);
-            const u32x4 vw = __builtin_amdgcn_raw_buffer_load_b128(vin, off, 0, 0);
-            *(u32x4*)&k_lds[key * KP + c] = kw;
-            const vec8 vv = __builtin_bit_cast(vec8, vw);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) vt_lds[(c + j) * VP + key] = vv[j];
-        }
-        __syncthreads();
-        if (kb >= wave_end) continue;  // this wavefront's rows need no key of the block
+    // Pipeline: global loads run two blocks ahead of the computation, LDS writes one block
+    // ahead; one barrier per block separates the writes of a buffer from its readers.
+    fetch(0);
+    stage(0);
+    if (BN < kv_end) fetch(BN);
+    __syncthreads();
+    for (int kb = 0, buf = 0; kb < kv_end; kb += BN, buf ^= 1) {
+        if (kb < wave_end) {  // else this wavefront's rows need no key of the block
 
-        // S^T[key][row] for the 32 keys of the block
-        f32x16 s = f32x16{};
+        // S^T[key][row] for the 32-key tiles of the block that this wavefront needs
+        constexpr int NS = BN / 32;
+        f32x16 s[NS];
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-            const vec8 kf = *(const vec8*)&k_lds[(lane & 31) * KP + 16 * kk + 8 * g];
-            s = MF::mfma(kf, qf[kk], s);
-        }
-        // mask, scale, block max of the row
-        float z[16];
-        float mb = -INFINITY;
+        for (int st = 0; st < NS; ++st) {
+            s[st] = f32x16{};
+            if (st == 0 || kb + 32 * st < wave_end) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int key = kb + 8 * (e / 4) + 4 * g + (e & 3);
-            z[e] = (key <= row && key < L) ? s[e] * a.k2 : -INFINITY;
-            mb = fmaxf(mb, z[e]);
-        }
-        mb = fmaxf(mb, swap_halves(mb));
-        const float m_new = fmaxf(m_run, mb);
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_use);
-        m_run = m_new;
-        // probabilities, rounded to the element type for the second product
-        vec8 p[2];
-        float ps = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const float pe = __builtin_amdgcn_exp2f(z[e] - m_use);
-            ps += pe;
-            p[e / 8][e % 8] = (elem_t)pe;
-        }
-        l_part = l_part * alpha + ps;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] *= alpha;
-        // O^T[d][row] += V^T[d][keys] P^T[keys][row]; half h covers the lane's e = 8h..8h+7,
-        // that is keys 16h + 8*(j/4) + 4*g + j%4 for j = 0..7
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const elem_t* vr = &vt_lds[(32 * t + (lane & 31)) * VP + 16 * h + 4 * g];
-                const vec4 v0 = *(const vec4*)vr, v1 = *(const vec4*)(vr + 8);
-                const vec8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-                acc[t] = MF::mfma(vf, p[h], acc[t]);
+                for (int kk = 0; kk < D / 16; ++kk) {
+                    const vec8 kf =
+                        *(const vec8*)&k_lds[buf][(32 * st + (lane & 31)) * KP + 16 * kk + 8 * g];
+                    s[st] = MF::mfma(kf, qf[kk], s[st]);
+                }
             }
         }
+        // z = s * k2 (k2 = |scale| * log2 e >= 0). The row max is taken on the raw scores,
+        // so that each probability costs one fma and one exp: p = 2^(s*k2 - m). Masked keys
+        // (only in blocks that reach the wavefront's diagonal or the length) get s = -inf.
+        if (!(kb + BN - 1 <= row_lo && kb + BN <= L)) {  // uniform over the wavefront
+            // key = kb + 4g + (32st + 8(e/4) + e%4) is kept when key <= min(row, L - 1)
+            const int lim = min(row, L - 1) - kb - 4 * g;
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    s[st][e] = 32 * st + 8 * (e / 4) + (e & 3) <= lim ? s[st][e] : -INFINITY;
+            }
+        }
+        float mb = -INFINITY;
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mb = fmaxf(mb, s[st][e]);
+        }
+        mb = fmaxf(mb, swap_halves(mb));
+        // running max in the log2 domain: m = max over kept keys of s * k2
+        const float m_new = fmaxf(m_run, mb == -INFINITY ? -INFINITY : mb * k2);
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_use);
+        const bool moved = m_new != m_run;
+        m_run = m_new;
+        // probabilities, rounded to the element type for the second product
+        vec8 p[2 * NS];
+        float ps = 0.0f;
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][e], k2, -m_use));
+                ps += pe;
+                p[2 * st + e / 8][e % 8] = (elem_t)pe;
+            }
+        }
+        // rescale the running sums only when some row's max moved (alpha = 1 otherwise)
+        if (__builtin_amdgcn_ballot_w64(moved)) {
+            l_part *= alpha;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[t] *= alpha;
+        }
+        l_part += ps;
+        // O^T[d][row] += V^T[d][keys] P^T[keys][row]; vector 2*st + h covers the lane's keys
+        // kb + 32*st + 16h + 8*(j/4) + 4*g + j%4, j = 0..7
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            if (st > 0 && kb + 32 * st >= wave_end) break;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    // keys 32st + 16h + 8*(j/4) + 4g + j%4 sit at columns 32st + 16h + 8g + j
+                    const vec8 vf = *(const vec8*)&vt_lds[buf][(32 * t + (lane & 31)) * VP +
+                                                               32 * st + 16 * h + 8 * g];
+                    acc[t] = MF::mfma(vf, p[2 * st + h], acc[t]);
+                }
+            }
+        }
+        }  // kb < wave_end
+        // the next block into the other buffer (its readers finished before the last
+        // barrier), then the loads of the block after it
+        if (kb + BN < kv_end) {
+            stage(buf ^ 1);
+            if (kb + 2 * BN < kv_end) fetch(kb + 2 * BN);
+        }
+        __syncthreads();
     }
 
     // normalise and store the rows below L (acc[t] register e: d = 32t + 8*(e/4) + 4g + e%4)

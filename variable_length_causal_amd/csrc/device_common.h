@@ -224,6 +224,15 @@ __device__ __forceinline__ uint32_t xcd_chunked(uint32_t bid, uint32_t nblk, uin
     return ((((i >> shift) * kXcds) + x) << shift) + (i & ((1u << shift) - 1u));
 }
 
+// The same renumbering with chunks of any size ch: XCD x takes chunks x, x + 8, ...
+__device__ __forceinline__ uint32_t xcd_grouped(uint32_t bid, uint32_t nblk, uint32_t ch) {
+    const uint32_t span = kXcds * ch;
+    const uint32_t full = nblk / span * span;
+    if (bid >= full) return bid;
+    const uint32_t x = bid % kXcds, i = bid / kXcds;
+    return ((i / ch) * kXcds + x) * ch + i % ch;
+}
+
 __device__ __forceinline__ int clamp_len(int32_t raw, int S) {
     return raw < 0 ? 0 : (raw > S ? S : raw);
 }
