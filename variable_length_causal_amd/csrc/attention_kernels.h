@@ -186,7 +186,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3
     if (BN < kv_end) fetch(BN);
     __syncthreads();
     for (int kb = 0, buf = 0; kb < kv_end; kb += BN, buf ^= 1) {
-        if (kb < wave_end) {  // else this wavefront's rows need no key of the block
+        {  // a wavefront whose rows need no key of the block computes it masked
 
         // S^T[key][row] for the 32-key tiles of the block that this wavefront needs
         constexpr int NS = BN / 32;
@@ -194,13 +194,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
             s[st] = f32x16{};
-            if (st == 0 || kb + 32 * st < wave_end) {
 #pragma unroll
-                for (int kk = 0; kk < D / 16; ++kk) {
-                    const vec8 kf =
-                        *(const vec8*)&k_lds[buf][(32 * st + (lane & 31)) * KP + 16 * kk + 8 * g];
-                    s[st] = MF::mfma(kf, qf[kk], s[st]);
-                }
+            for (int kk = 0; kk < D / 16; ++kk) {
+                const vec8 kf =
+                    *(const vec8*)&k_lds[buf][(32 * st + (lane & 31)) * KP + 16 * kk + 8 * g];
+                s[st] = MF::mfma(kf, qf[kk], s[st]);
             }
         }
         // z = s * k2 (k2 = |scale| * log2 e >= 0). The row max is taken on the raw scores,
@@ -227,7 +225,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3
         const float m_new = fmaxf(m_run, mb == -INFINITY ? -INFINITY : mb * k2);
         const float m_use = m_new == -INFINITY ? 0.0f : m_new;
         const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_use);
-        const bool moved = m_new != m_run;
         m_run = m_new;
         // probabilities, rounded to the element type for the second product
         vec8 p[2 * NS];
@@ -241,18 +238,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3
                 p[2 * st + e / 8][e % 8] = (elem_t)pe;
             }
         }
-        // rescale the running sums only when some row's max moved (alpha = 1 otherwise)
-        if (__builtin_amdgcn_ballot_w64(moved)) {
-            l_part *= alpha;
+        // rescale the running sums (alpha = 1 where the row's max did not move); done in
+        // place every block, which keeps the accumulators in the same registers
+        l_part = l_part * alpha + ps;
 #pragma unroll
-            for (int t = 0; t < NT; ++t) acc[t] *= alpha;
-        }
-        l_part += ps;
+        for (int t = 0; t < NT; ++t) acc[t] *= alpha;
         // O^T[d][row] += V^T[d][keys] P^T[keys][row]; vector 2*st + h covers the lane's keys
         // kb + 32*st + 16h + 8*(j/4) + 4*g + j%4, j = 0..7
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
-            if (st > 0 && kb + 32 * st >= wave_end) break;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
 #pragma unroll
