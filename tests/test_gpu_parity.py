@@ -282,3 +282,42 @@ def test_full_scaled_f16_32x1x4096():
 
 def test_full_skewed_bf16_8x32x8192():
     full_workload_check("skewed_bf16_8x32x8192", n_sample_rows=800)
+
+
+def test_side_stream_and_graph_replay():
+    """The binding launches on the caller's current stream (a side stream here), and a
+    captured HIP graph of forward + backward replays to the same bits as eager calls, with
+    eager work and synchronisations between the replays."""
+    S, lens = 520, [520, 300, 0]
+    x = workloads.scores_cpu((3, 2, S, S), workloads.F32, 1.0, 77).cuda()
+    dy = workloads.scores_cpu((3, 2, S, S), workloads.F32, 1.0, 78).cuda()
+    sl = torch.as_tensor(np.asarray(lens, np.int32)).cuda()
+    ref_y = g.forward(x, sl, 0.5)
+    ref_dx = g.backward(ref_y, dy, sl, 0.5)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    y = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        g.forward(x, sl, 0.5, out=y)
+        g.backward(y, dy, sl, 0.5, out=dx)
+    side.synchronize()
+    assert torch.equal(y.view(torch.int32), ref_y.view(torch.int32))
+    assert torch.equal(dx.view(torch.int32), ref_dx.view(torch.int32))
+    graph = torch.cuda.CUDAGraph()
+    y.fill_(float("nan"))
+    dx.fill_(float("nan"))
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        g.forward(x, sl, 0.5, out=y)
+        g.backward(y, dy, sl, 0.5, out=dx)
+    for i in range(3):
+        y.fill_(float("nan"))
+        dx.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), ref_y.view(torch.int32)), f"replay {i}"
+        assert torch.equal(dx.view(torch.int32), ref_dx.view(torch.int32)), f"replay {i}"
+        g.forward(x, sl, 0.25)   # eager work between replays
+        torch.cuda.synchronize()
