@@ -82,6 +82,8 @@ class Oracle:
         lib.gtms_oracle_rows_f64.restype = i32
         lib.gtms_oracle_backward_f64.argtypes = [p, p, p, p, i64, i64, i64, f32, i32]
         lib.gtms_oracle_backward_f64.restype = i32
+        lib.gtms_oracle_backward_rows_f64.argtypes = [p, p, p, p, p, i64, i64, f32, i32]
+        lib.gtms_oracle_backward_rows_f64.restype = i32
         lib.gtms_oracle_band_f64.argtypes = [p, p, p, i64, i64, i64, i64, i64, f32, i32]
         lib.gtms_oracle_band_f64.restype = i32
         lib.gtms_oracle_band_backward_f64.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, f32,
@@ -161,6 +163,24 @@ class Oracle:
         self._status(self.lib.gtms_oracle_backward_f64(_ptr(y), _ptr(dy), _ptr(dx), _ptr(sl),
                                                        B, M, S, scale, dtype),
                      "gtms_oracle_backward_f64")
+        return dx
+
+    def backward_rows_f64(self, y_rows: np.ndarray, dy_rows: np.ndarray, row_index, seq_len,
+                          scale: float = 1.0, dtype: int = F32) -> np.ndarray:
+        """fp64 gradients for independent rows: y_rows[i] and dy_rows[i] (length S) are row
+        row_index[i] of a plane whose batch has raw valid length seq_len[i]."""
+        y_rows = _check(y_rows, dtype)
+        dy_rows = _check(dy_rows, dtype)
+        n, S = y_rows.shape
+        assert dy_rows.shape == (n, S)
+        ri = np.ascontiguousarray(np.asarray(row_index, dtype=np.int64))
+        sl = _lens(seq_len, n)
+        assert ri.shape == (n,)
+        dx = np.empty((n, S), dtype=np.float64)
+        self._status(self.lib.gtms_oracle_backward_rows_f64(_ptr(y_rows), _ptr(dy_rows),
+                                                            _ptr(dx), _ptr(ri), _ptr(sl), n, S,
+                                                            scale, dtype),
+                     "gtms_oracle_backward_rows_f64")
         return dx
 
     # ---- mask variants: seq_lens may be None (every valid length is S)
@@ -290,6 +310,10 @@ def softmax_rows_f64(*a, **k):
 
 def backward_f64(*a, **k):
     return default().backward_f64(*a, **k)
+
+
+def backward_rows_f64(*a, **k):
+    return default().backward_rows_f64(*a, **k)
 
 
 def decode(bits: int, dtype: int) -> float:

@@ -268,6 +268,20 @@ int gtms_oracle_rows_f64(const void* rows_in, double* rows_out, const int64_t* r
  *   dx_j = scale * sum_i g_i y_i (delta_ij - y_j) = scale * y_j * (g_j - sum_i g_i y_i),
  * the sums running over the kept columns of the row. Masked elements and padded rows do
  * not reach the output, so their gradient is zero. */
+static void backward_row(const void* y, const void* dy, int64_t off, int64_t r, int64_t L,
+                         int64_t S, double scale, int dtype, double* dx) {
+    double dot = 0.0;
+    for (int64_t c = 0; c < S; ++c) {
+        if (kept(r, c, L)) dot += load_elem(dy, off + c, dtype) * load_elem(y, off + c, dtype);
+    }
+    for (int64_t c = 0; c < S; ++c) {
+        if (kept(r, c, L))
+            dx[c] = scale * load_elem(y, off + c, dtype) * (load_elem(dy, off + c, dtype) - dot);
+        else
+            dx[c] = 0.0;
+    }
+}
+
 int gtms_oracle_backward_f64(const void* y, const void* dy, double* dx,
                              const int32_t* seq_lens, int64_t B, int64_t M, int64_t S,
                              float scale, int dtype) {
@@ -280,20 +294,27 @@ int gtms_oracle_backward_f64(const void* y, const void* dy, double* dx,
         for (int64_t m = 0; m < M; ++m) {
             for (int64_t r = 0; r < S; ++r) {
                 int64_t off = ((b * M + m) * S + r) * S;
-                double dot = 0.0;
-                for (int64_t c = 0; c < S; ++c) {
-                    if (kept(r, c, L))
-                        dot += load_elem(dy, off + c, dtype) * load_elem(y, off + c, dtype);
-                }
-                for (int64_t c = 0; c < S; ++c) {
-                    if (kept(r, c, L))
-                        dx[off + c] = (double)scale * load_elem(y, off + c, dtype) *
-                                      (load_elem(dy, off + c, dtype) - dot);
-                    else
-                        dx[off + c] = 0.0;
-                }
+                backward_row(y, dy, off, r, L, S, (double)scale, dtype, dx + off);
             }
         }
+    }
+    return OK;
+}
+
+int gtms_oracle_backward_rows_f64(const void* y_rows, const void* dy_rows, double* dx_rows,
+                                  const int64_t* row, const int32_t* seq_len, int64_t nrows,
+                                  int64_t S, float scale, int dtype) {
+    int ebits, pbits, bytes;
+    if (!format_of(dtype, &ebits, &pbits, &bytes)) return ERR_DTYPE;
+    if (nrows < 0 || S < 0) return ERR_ARG;
+    if (nrows == 0 || S == 0) return OK;
+    if (!y_rows || !dy_rows || !dx_rows || !row || !seq_len) return ERR_ARG;
+    for (int64_t i = 0; i < nrows; ++i) {
+        if (row[i] < 0 || row[i] >= S) return ERR_ARG;
+    }
+    for (int64_t i = 0; i < nrows; ++i) {
+        backward_row(y_rows, dy_rows, i * S, row[i], valid_length(seq_len[i], S), S,
+                     (double)scale, dtype, dx_rows + i * S);
     }
     return OK;
 }

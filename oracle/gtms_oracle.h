@@ -39,6 +39,13 @@ int gtms_oracle_backward_f64(const void* y, const void* dy, double* dx,
                              const int32_t* seq_lens, int64_t B, int64_t M, int64_t S,
                              float scale, int dtype);
 
+/* Backward of independent rows: y_rows and dy_rows hold nrows rows of S elements; row i is
+ * row index row[i] of a plane whose batch has raw length seq_len[i]. dx_rows receives
+ * nrows*S fp64 results. */
+int gtms_oracle_backward_rows_f64(const void* y_rows, const void* dy_rows, double* dx_rows,
+                                  const int64_t* row, const int32_t* seq_len, int64_t nrows,
+                                  int64_t S, float scale, int dtype);
+
 /* Mask variants (ScaledMaskSoftmax article, sections 2.1, 4.1 and 6). A row's softmax runs
  * over its kept elements only; a row with no kept element is all zeros. seq_lens may be
  * NULL, meaning every valid length is S; otherwise element (r, c) needs r < L_b and c < L_b.

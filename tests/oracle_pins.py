@@ -452,6 +452,47 @@ def pin_backward(orc):
         assert abs(dx[b, m, r, j] - fd) <= 2e-5, (b, m, r, j, dx[b, m, r, j], fd)
 
 
+def pin_backward_rows(orc):
+    """The backward's row entry point gives the same bits as the full tensor; NaN and
+    infinity outside a row's kept prefix change nothing; on rows of 3000 elements it agrees
+    with central finite differences of the forward's row entry point."""
+    rng = np.random.default_rng(25)
+    S = 19
+    lens = np.array([S, 8, -3], dtype=np.int32)
+    y = rng.uniform(size=(3, 2, S, S)).astype(np.float32)
+    g = rng.normal(size=(3, 2, S, S)).astype(np.float32)
+    full = orc.backward_f64(y, g, lens, 0.7, F32)
+    idx = [(b, m, r) for b in range(3) for m in range(2) for r in range(S)]
+    pick = [idx[i] for i in rng.choice(len(idx), size=40, replace=False)]
+    yr = np.stack([y[b, m, r] for b, m, r in pick])
+    gr = np.stack([g[b, m, r] for b, m, r in pick])
+    ri, li = [r for _, _, r in pick], [lens[b] for b, _, _ in pick]
+    got = orc.backward_rows_f64(yr, gr, ri, li, 0.7, F32)
+    for i, (b, m, r) in enumerate(pick):
+        assert np.array_equal(got[i], full[b, m, r])
+    for i, (b, m, r) in enumerate(pick):
+        L = min(max(int(lens[b]), 0), S)
+        off = np.array([not _kept(r, c, L) for c in range(S)])
+        yr[i][off], gr[i][off] = np.float32("nan"), np.float32("inf")
+    assert np.array_equal(orc.backward_rows_f64(yr, gr, ri, li, 0.7, F32), got)
+    # long rows: f(x) = sum(g * softmax(x)), step exact in binary32
+    S, L, scale, h = 3000, 2500, 0.8, 2.0 ** -10
+    for r in (0, 1234, 2499):
+        x = rng.normal(0.0, 2.0, size=(1, S)).astype(np.float32)
+        g1 = rng.normal(size=(1, S)).astype(np.float32)
+        y1 = orc.softmax_rows_f64(x, [r], [L], scale, F32).astype(np.float32)
+        dx = orc.backward_rows_f64(y1, g1, [r], [L], scale, F32)[0]
+        assert not dx[r + 1:].any()
+        gd = g1.astype(np.float64)
+        for j in sorted({0, r // 2, r}):
+            xp, xm = x.copy(), x.copy()
+            xp[0, j] += np.float32(h)
+            xm[0, j] -= np.float32(h)
+            fd = (float((gd * orc.softmax_rows_f64(xp, [r], [L], scale, F32)).sum()) -
+                  float((gd * orc.softmax_rows_f64(xm, [r], [L], scale, F32)).sum())) / (2 * h)
+            assert abs(dx[j] - fd) <= 1e-9 + 1e-5 * abs(fd), (r, j, dx[j], fd)
+
+
 # ------------------------------------------------------------------------ mask variants
 # The ScaledMaskSoftmax article ("优化ScaledMaskSoftmax算子") masks scores with minus infinity
 # before the softmax (section 2.1), zeroes rows whose every element is masked (section
@@ -709,6 +750,7 @@ ALL_PINS = [
     pin_printed_masks, pin_printed_output, pin_row0, pin_row_sums, pin_exact_zeros,
     pin_brute_force, pin_closed_forms, pin_shift_and_scale, pin_masked_poison,
     pin_length_edges, pin_codec, pin_rounded_outputs, pin_rows_api, pin_backward,
+    pin_backward_rows,
     pin_band_brute_force, pin_band_closed_forms, pin_masked_brute_force, pin_variant_backward,
     pin_attention,
 ]

@@ -28,8 +28,11 @@ MUTATIONS = {
                          "mag = ldexp((double)f, -bias - pbits);"),
     "backward_sign": ("(load_elem(dy, off + c, dtype) - dot);",
                       "(load_elem(dy, off + c, dtype) + dot);"),
-    "backward_scale_dropped": ("dx[off + c] = (double)scale * load_elem(y, off + c, dtype) *",
-                               "dx[off + c] = load_elem(y, off + c, dtype) *"),
+    "backward_scale_dropped": ("dx[c] = scale * load_elem(y, off + c, dtype) *",
+                               "dx[c] = load_elem(y, off + c, dtype) *"),
+    "backward_dot_unmasked": ("if (kept(r, c, L)) dot += load_elem(dy", "dot += load_elem(dy"),
+    "backward_rows_row_ignored": ("backward_row(y_rows, dy_rows, i * S, row[i],",
+                                  "backward_row(y_rows, dy_rows, i * S, S - 1,"),
     "row_column_swapped": ("if (kept(r, c, L))\n            y[c]",
                            "if (kept(c, r, L))\n            y[c]"),
     # mask variants
