@@ -373,7 +373,10 @@ def main():
         },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline and args.op == "forward" and args.variant == "tril":
+    # the CPU oracle runs whole planes; planes beyond 2^26 elements (the 65536-wide rows) would
+    # take minutes and tens of GB of host memory, so their lines carry no baseline
+    if not args.no_cpu_baseline and args.op == "forward" and args.variant == "tril" \
+            and w.S * w.S <= (1 << 26):
         out["cpu_baseline"] = cpu_baseline(xs[0], lens, w, args.cpu_budget)
     print(json.dumps(out), flush=True)
 

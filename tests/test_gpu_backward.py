@@ -89,6 +89,43 @@ def test_backward_long_rows():
             run_case((len(lens), 1, S, S), dtype, lens, 0.125, path, seed=200 + S)
 
 
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DNAME[d])
+def test_backward_widest_wave_rows(dtype):
+    """Rows of 4000 elements on the one-wavefront path: sixteen binary32 or eight 16-bit
+    vectors per lane, the largest layouts of that path."""
+    run_case((2, 1, 4000, 4000), dtype, [4000, 1401], 0.6, "wave", seed=400)
+
+
+def test_backward_block_rows_sampled():
+    """Rows that fill the block path's registers (binary16 40000 and bfloat16 65536 at eight
+    16-byte vectors per lane, binary32 65536 forced to sixteen), y uniform in [0, 2/L) (rows
+    that sum to about 1, like the forward's outputs the error bound is derived for), dy
+    normal; sampled rows against the oracle's row entry point."""
+    for dtype, S, path in ((workloads.F16, 40000, "auto"), (workloads.BF16, 65536, "auto"),
+                           (workloads.F32, 65536, "block")):
+        L = S - 17
+        print(f"backward block rows S={S} dtype={DNAME[dtype]} path={path}", flush=True)
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(S)
+        # uniform in [0, 2/L): a row sums to about 1, as a forward output does
+        y = torch.rand((1, 1, S, S), generator=gen, device="cuda").mul_(2.0 / L).to(
+            workloads.torch_dtype(dtype))
+        dy = workloads.scores_device((1, 1, S, S), dtype, 1.0, S + 1)
+        sl = torch.as_tensor(np.asarray([L], dtype=np.int32)).cuda()
+        dx = g.backward(y, dy, sl, 0.3, path=path)
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(S)
+        rs = sorted(set(int(r) for r in rng.choice(L, 12, replace=False)) |
+                    {0, L // 2, L - 1, L, S - 1})
+        y_st = workloads.to_storage(torch.stack([y[0, 0, r] for r in rs]).cpu())
+        g_st = workloads.to_storage(torch.stack([dy[0, 0, r] for r in rs]).cpu())
+        d_st = workloads.to_storage(torch.stack([dx[0, 0, r] for r in rs]).cpu())
+        ref = oracle.backward_rows_f64(y_st, g_st, rs, [L] * len(rs), 0.3, dtype)
+        check_rows(d_st, ref, y_st, g_st, [L] * len(rs), rs, 0.3, dtype)
+        del y, dy, dx
+        torch.cuda.empty_cache()
+
+
 def test_backward_in_place_and_poison():
     """dx written over dy gives the same bits; NaN in masked cells of y and dy changes
     nothing."""

@@ -321,3 +321,38 @@ def test_side_stream_and_graph_replay():
         assert torch.equal(dx.view(torch.int32), ref_dx.view(torch.int32)), f"replay {i}"
         g.forward(x, sl, 0.25)   # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_full_long_bf16_2x2x65536():
+    """Rows of 65536 bfloat16 elements (the block path at eight 16-byte vectors per lane) at
+    the benchmark's size: sampled rows against the oracle, and on every row, in chunks of rows,
+    exact zeros past the kept prefix and kept rows that sum to 1."""
+    name = "long_bf16_2x2x65536"
+    w = workloads.WORKLOADS[name]
+    lens = workloads.seq_lens(w)
+    print(f"full workload {name} lens={list(lens)}", flush=True)
+    x = workloads.scores_device(w.shape, w.dtype, w.sigma, w.x_seed)
+    y = g.forward(x, torch.as_tensor(lens).cuda(), w.scale)
+    torch.cuda.synchronize()
+    B, M, S, _ = w.shape
+    rng = np.random.default_rng(w.x_seed)
+    rows = [(b, int(rng.integers(M)), r) for b in range(B)
+            for r in {0, int(lens[b]) - 1, min(int(lens[b]), S - 1), S - 1}]
+    rows += [(int(rng.integers(B)), int(rng.integers(M)), int(rng.integers(S))) for _ in range(60)]
+    worst = sample_rows_check(x, y, lens, w.scale, w.dtype, rows)
+    col = torch.arange(S, device="cuda")
+    for b in range(B):
+        L = int(lens[b])
+        for m in range(M):
+            for r0 in range(0, S, 2048):
+                blk = y[b, m, r0:r0 + 2048]
+                r = torch.arange(r0, r0 + blk.shape[0], device="cuda")
+                masked = (col[None, :] > r[:, None]) | (r[:, None] >= L)
+                assert not (blk.view(torch.int16)[masked] != 0).any(), (b, m, r0)
+                kept = int(max(0, min(L, r0 + blk.shape[0]) - r0))
+                if kept:
+                    sums = blk[:kept].float().sum(dim=1)
+                    assert float((sums - 1).abs().max()) <= 1.6e-2, (b, m, r0)
+    print(f"{name}: worst sampled error {worst:.3g}", flush=True)
+    del x, y
+    torch.cuda.empty_cache()

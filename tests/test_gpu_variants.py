@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 import workloads
-from gtms_check import TOL, bits, path_ok, to_f64
+from gtms_check import TOL, bits, kept_row, path_ok, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -244,6 +244,100 @@ def test_variant_backward(dtype):
             torch.cuda.synchronize()
             grad_check(dxb, refb, yb, dy, keep_b, 0.9, dtype, f"band bwd S={S} {path}")
             grad_check(dxm, refm, ym, dy, keep_m, 0.9, dtype, f"masked bwd S={S} {path}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DNAME[d])
+def test_variants_widest_wave_rows(dtype):
+    """Band and explicit mask, forward and backward, on rows of 4000 elements through the
+    one-wavefront path: sixteen binary32 or eight 16-bit vectors per lane, the largest
+    layouts of that path (random masks, one all-masked row, a shorter second sample)."""
+    S, lens, scale = 4000, [4000, 1401], 0.9
+    rng = np.random.default_rng(71)
+    mask = (rng.uniform(size=(2, 1, S, S)) < 0.5).astype(np.uint8)
+    mask[0, 0, 100, :] = 0
+    band_case((2, 1, S, S), dtype, lens, -1500, 7, scale, ("wave",), seed=72)
+    masked_case((2, 1, S, S), dtype, mask, lens, scale, ("wave",), seed=73)
+    x = workloads.to_storage(workloads.scores_cpu((2, 1, S, S), dtype, 1.0, 74))
+    dy = workloads.to_storage(workloads.scores_cpu((2, 1, S, S), dtype, 1.0, 75))
+    tdt = workloads.torch_dtype(dtype)
+    yb = workloads.to_storage(torch.as_tensor(
+        oracle.softmax_band_f64(x, lens, -1500, 7, scale, dtype)).to(tdt))
+    ym = workloads.to_storage(torch.as_tensor(
+        oracle.softmax_masked_f64(x, mask, lens, scale, dtype)).to(tdt))
+    keep_b = np.stack([band_keep(S, L, -1500, 7)[None] for L in lens])
+    keep_m = expand_mask(mask, 2, 1, S) & np.stack([length_keep(S, L)[None] for L in lens])
+    sl = lens_dev(lens)
+    dyd = workloads.from_storage(dy, dtype).cuda()
+    print(f"variant backward S={S} {DNAME[dtype]} path=wave", flush=True)
+    dxb = g.backward_band(workloads.from_storage(yb, dtype).cuda(), dyd, sl, -1500, 7, scale,
+                          path="wave")
+    dxm = g.backward_masked(workloads.from_storage(ym, dtype).cuda(), dyd,
+                            torch.as_tensor(mask).cuda(), sl, scale, path="wave")
+    torch.cuda.synchronize()
+    grad_check(dxb, oracle.band_backward_f64(yb, dy, lens, -1500, 7, scale, dtype), yb, dy,
+               keep_b, scale, dtype, "band bwd wave")
+    grad_check(dxm, oracle.masked_backward_f64(ym, dy, mask, lens, scale, dtype), ym, dy,
+               keep_m, scale, dtype, "masked bwd wave")
+
+
+def test_variants_block_rows_sampled():
+    """Rows that fill the block path's registers (binary16 40000, bfloat16 65536: eight
+    16-byte vectors per lane). A band [-S, 0] and a lower-triangular mask of ones, both
+    with the valid length, keep exactly the grouped tril set, so sampled rows compare with
+    the oracle's tril row entry points, forward and backward."""
+    for dtype, S in ((workloads.F16, 40000), (workloads.BF16, 65536)):
+        L = S - 17
+        print(f"variant block rows S={S} {DNAME[dtype]}", flush=True)
+        sl = lens_dev([L])
+        tril = torch.ones((S, S), dtype=torch.uint8, device="cuda").tril_()[None, None]
+        rng = np.random.default_rng(S)
+        rs = sorted(set(int(r) for r in rng.choice(L, 10, replace=False)) |
+                    {0, L // 2, L - 1, L, S - 1})
+
+        def rows_of(t):
+            return workloads.to_storage(torch.stack([t[0, 0, r] for r in rs]).cpu())
+
+        def check_fwd(out, xs, tag):
+            ref = oracle.softmax_rows_f64(xs, rs, [L] * len(rs), 0.5, dtype)
+            st = rows_of(out)
+            keep = np.stack([kept_row(S, L, r) for r in rs])
+            assert not bits(st)[~keep].any(), tag
+            err = np.abs(to_f64(st, dtype) - ref)[keep]
+            assert float(err.max()) <= TOL[dtype], (tag, float(err.max()))
+
+        x = workloads.scores_device((1, 1, S, S), dtype, 1.0, S + 2)
+        xs = rows_of(x)
+        check_fwd(g.forward_band(x, sl, -S, 0, 0.5), xs, "band")
+        check_fwd(g.forward_masked(x, tril, sl, 0.5), xs, "masked")
+        del x
+        torch.cuda.empty_cache()
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(S)
+        # uniform in [0, 2/L): a row sums to about 1, as a forward output does
+        y = torch.rand((1, 1, S, S), generator=gen, device="cuda").mul_(2.0 / L).to(
+            workloads.torch_dtype(dtype))
+        dy = workloads.scores_device((1, 1, S, S), dtype, 1.0, S + 3)
+        ys, gs = rows_of(y), rows_of(dy)
+        ref = oracle.backward_rows_f64(ys, gs, rs, [L] * len(rs), 0.5, dtype)
+        keep = np.stack([kept_row(S, L, r) for r in rs])
+        for tag, run in (("band bwd", lambda: g.backward_band(y, dy, sl, -S, 0, 0.5)),
+                         ("masked bwd", lambda: g.backward_masked(y, dy, tril, sl, 0.5))):
+            dx = run()
+            torch.cuda.synchronize()
+            grad_check_rows(rows_of(dx), ref, ys, gs, keep, 0.5, dtype, tag)
+            del dx
+        del y, dy, tril
+        torch.cuda.empty_cache()
+
+
+def grad_check_rows(st, ref, y_st, dy_st, keep, scale, dtype, tag):
+    """grad_check on sampled rows ([n, S] arrays)."""
+    assert not bits(st)[~keep].any(), f"{tag}: nonzero bits outside the kept set"
+    got, yv, gv = to_f64(st, dtype), to_f64(y_st, dtype), to_f64(dy_st, dtype)
+    gmax = np.max(np.where(keep, np.abs(gv), 0.0), axis=-1, keepdims=True)
+    bound = U[dtype] * np.abs(ref) + 1e-5 * abs(scale) * yv * gmax + TINY[dtype]
+    err = np.abs(got - ref)
+    assert np.all(err[keep] <= bound[keep]), f"{tag}: {float(np.max((err - bound)[keep]))}"
 
 
 def sampled_rows(x_dev, y_dev, rows, ref_row, dtype):

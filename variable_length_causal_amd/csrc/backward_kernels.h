@@ -18,7 +18,9 @@
 
 namespace gtms {
 
-template <class IO, int NA, int STRIDE, int MK>
+// LEAN (kernels with NV * VEC >= kLeanElems) as for the forward row parts; here it also makes
+// the output pass unpack y and g again instead of keeping the fp32 copies that dot() made.
+template <class IO, int NA, int STRIDE, int MK, bool LEAN>
 struct GradPart {
     using MIO = MaskIo<IO::VEC>;
     typename IO::raw_t ry[NA], rg[NA];
@@ -32,9 +34,15 @@ struct GradPart {
     __device__ __forceinline__ static int kept_from(int t, int j, int hv, const Cols& k) {
         return MK == MK_TRIL ? 0 : k.c0 - (t + j * STRIDE - hv) * IO::VEC;
     }
-    __device__ __forceinline__ bool kept(int j, int q, int ka, int kc) const {
+    // The mask bytes of slot j (a placeholder for the other mask kinds).
+    __device__ __forceinline__ typename MIO::raw_t mask_of(int j) const {
+        if constexpr (MK == MK_MASK) return mk[j];
+        else return typename MIO::raw_t{};
+    }
+    __device__ __forceinline__ static bool kept(const typename MIO::raw_t& mb, int q, int ka,
+                                                int kc) {
         bool r = q < kc && (MK == MK_TRIL || q >= ka);
-        if constexpr (MK == MK_MASK) r = r && MIO::kept(mk[j], q);
+        if constexpr (MK == MK_MASK) r = r && MIO::kept(mb, q);
         return r;
     }
 
@@ -57,11 +65,12 @@ struct GradPart {
 #pragma unroll
         for (int j = 0; j < NA; ++j) {
             const int kc = kept_count(t, j, hv, k), ka = kept_from(t, j, hv, k);
+            const auto mb = mask_of(j);
             float fy[VEC], fg[VEC];
             IO::unpack(ry[j], fy);
             IO::unpack(rg[j], fg);
 #pragma unroll
-            for (int q = 0; q < VEC; ++q) d += kept(j, q, ka, kc) ? fy[q] * fg[q] : 0.0f;
+            for (int q = 0; q < VEC; ++q) d += kept(mb, q, ka, kc) ? fy[q] * fg[q] : 0.0f;
         }
     }
 
@@ -71,13 +80,16 @@ struct GradPart {
         constexpr int VEC = IO::VEC;
 #pragma unroll
         for (int j = 0; j < NA; ++j) {
-            const int kc = kept_count(t, j, hv, k), ka = kept_from(t, j, hv, k);
+            const int kc = fresh_if<LEAN>(kept_count(t, j, hv, k)),
+                      ka = fresh_if<LEAN>(kept_from(t, j, hv, k));
+            const auto mb = mask_of(j);
+            const typename IO::raw_t y = fresh_if<LEAN>(ry[j]), g = fresh_if<LEAN>(rg[j]);
             float fy[VEC], fg[VEC], o[VEC];
-            IO::unpack(ry[j], fy);
-            IO::unpack(rg[j], fg);
+            IO::unpack(y, fy);
+            IO::unpack(g, fg);
 #pragma unroll
             for (int q = 0; q < VEC; ++q)
-                o[q] = kept(j, q, ka, kc) ? scale * fy[q] * (fg[q] - D) : 0.0f;
+                o[q] = kept(mb, q, ka, kc) ? scale * fy[q] * (fg[q] - D) : 0.0f;
             IO::template store<SP>(out, (t + j * STRIDE) * IO::BYTES, IO::pack(o));
         }
     }
@@ -113,7 +125,7 @@ __device__ __forceinline__ void bwd_wave_row(const FwdArgs& a, uint32_t plane, i
     const GradRows in = grad_rows<IO, MK>(a, plane, r, nin);
     const int hv = sp.hv;
     with_live_slots<NV>((nin + hv + kWave - 1) / kWave, [&]<int NA>() {
-        GradPart<IO, NA, kWave, MK> p;
+        GradPart<IO, NA, kWave, MK, NV * IO::VEC >= kLeanElems> p;
         p.load(in.y, in.g, in.m, lane, hv, k);
         write_zero_slots<IO, NA, NV, kWave, SP>(out, lane);
         p.dot(lane, hv, k);
@@ -155,7 +167,7 @@ __device__ __forceinline__ void bwd_block_row(const FwdArgs& a, uint32_t plane, 
     const GradRows in = grad_rows<IO, MK>(a, plane, r, nin);
     const int hv = sp.hv;
     with_live_slots<NV>((nin + hv + T - 1) / T, [&]<int NA>() {
-        GradPart<IO, NA, T, MK> p;
+        GradPart<IO, NA, T, MK, NV * IO::VEC >= kLeanElems> p;
         p.load(in.y, in.g, in.m, t, hv, k);
         write_zero_slots<IO, NA, NV, T, SP>(out, t);
         p.dot(t, hv, k);

@@ -239,4 +239,15 @@ __device__ __forceinline__ int clamp_len(int32_t raw, int S) {
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Hides a register value from the optimiser (an empty asm that claims to rewrite it), so that
+// values derived from it before this point are recomputed rather than kept live after it. The
+// row kernels use it so that neither the unpacked fp32 copy of a packed 16-bit row (twice its
+// registers) nor the per-element keep conditions (one 64-bit lane mask in scalar registers
+// each) live across a loop or a reduction: recomputing either costs one instruction.
+template <class T> __device__ __forceinline__ void opaque(T& v) { asm volatile("" : "+v"(v)); }
+template <bool ON, class T> __device__ __forceinline__ T fresh_if(T v) {
+    if constexpr (ON) opaque(v);
+    return v;
+}
+
 }  // namespace gtms

@@ -201,9 +201,17 @@ __device__ __forceinline__ Span row_span(const FwdArgs& a, uint32_t plane, int r
 // ColossalAI's flash_decoding.py does (_flash_decoding_fwd_reduce_kernel):
 //   M = max_t m_t,  S = sum_t s_t * 2^(m_t - M),  y = e * 2^(m_t - M) / S,
 // so each element costs one exp. A thread without kept columns has m_t = -inf, s_t = 0.
+//
+// LEAN is set by kernels whose lanes hold 64 or more elements (NV * VEC >= 64). The keep
+// conditions of the output pass are then rebuilt from opaque copies of their inputs (see
+// opaque()) instead of being kept live across the reduction: at that size they no longer fit
+// in scalar registers and spill. Smaller kernels run faster without it.
 constexpr int kOutOfRange = (int)0x80000000u;  // an offset every buffer range check rejects
 
-template <class IO, int NA, int STRIDE, int MK>
+// Lanes holding this many elements or more run the LEAN variants of the row parts.
+constexpr int kLeanElems = 64;
+
+template <class IO, int NA, int STRIDE, int MK, bool LEAN>
 struct RowPart {
     using MIO = MaskIo<IO::VEC>;
     typename IO::raw_t raw[NA];
@@ -220,9 +228,15 @@ struct RowPart {
     __device__ __forceinline__ static int kept_from(int t, int j, int hv, const Cols& k) {
         return MK == MK_TRIL ? 0 : k.c0 - (t + j * STRIDE - hv) * IO::VEC;
     }
-    __device__ __forceinline__ bool kept(int j, int q, int ka, int kc) const {
+    // The mask bytes of slot j (a placeholder for the other mask kinds).
+    __device__ __forceinline__ typename MIO::raw_t mask_of(int j) const {
+        if constexpr (MK == MK_MASK) return mk[j];
+        else return typename MIO::raw_t{};
+    }
+    __device__ __forceinline__ static bool kept(const typename MIO::raw_t& mb, int q, int ka,
+                                                int kc) {
         bool r = q < kc && (MK == MK_TRIL || q >= ka);
-        if constexpr (MK == MK_MASK) r = r && MIO::kept(mk[j], q);
+        if constexpr (MK == MK_MASK) r = r && MIO::kept(mb, q);
         return r;
     }
 
@@ -245,11 +259,12 @@ struct RowPart {
 #pragma unroll
         for (int j = 0; j < NA; ++j) {
             const int kc = kept_count(t, j, hv, k), ka = kept_from(t, j, hv, k);
+            const auto mb = mask_of(j);
             float f[VEC];
             IO::unpack(raw[j], f);
 #pragma unroll
             for (int q = 0; q < VEC; ++q) {
-                e[j][q] = kept(j, q, ka, kc) ? f[q] * kscale : -INFINITY;
+                e[j][q] = kept(mb, q, ka, kc) ? f[q] * kscale : -INFINITY;
                 m = fmaxf(m, e[j][q]);
             }
         }
@@ -257,10 +272,16 @@ struct RowPart {
         const float mm = m == -INFINITY ? 0.0f : m;  // keeps 2^(-inf - mm) = 0 well defined
 #pragma unroll
         for (int j = 0; j < NA; ++j) {
+            const int kc = kept_count(t, j, hv, k), ka = kept_from(t, j, hv, k);
+            const auto mb = mask_of(j);
 #pragma unroll
             for (int q = 0; q < VEC; ++q) {
-                e[j][q] = __builtin_amdgcn_exp2f(e[j][q] - mm);
-                s += e[j][q];
+                const float x = __builtin_amdgcn_exp2f(e[j][q] - mm);
+                s += x;
+                // LEAN explicit mask: a dropped element is marked by a negative e (no kept e
+                // is negative, a NaN compares false), so the mask bytes need not stay live.
+                if constexpr (MK == MK_MASK && LEAN) e[j][q] = kept(mb, q, ka, kc) ? x : -1.0f;
+                else e[j][q] = x;
             }
         }
     }
@@ -285,10 +306,15 @@ struct RowPart {
         constexpr int VEC = IO::VEC;
 #pragma unroll
         for (int j = 0; j < NA; ++j) {
-            const int kc = kept_count(t, j, hv, k), ka = kept_from(t, j, hv, k);
+            const int kc = fresh_if<LEAN>(kept_count(t, j, hv, k)),
+                      ka = fresh_if<LEAN>(kept_from(t, j, hv, k));
+            const auto mb = mask_of(j);
             float f[VEC];
 #pragma unroll
-            for (int q = 0; q < VEC; ++q) f[q] = kept(j, q, ka, kc) ? e[j][q] * g : 0.0f;
+            for (int q = 0; q < VEC; ++q) {
+                if constexpr (MK == MK_MASK && LEAN) f[q] = e[j][q] < 0.0f ? 0.0f : e[j][q] * g;
+                else f[q] = kept(mb, q, ka, kc) ? e[j][q] * g : 0.0f;
+            }
             IO::template store<SP>(out, (t + j * STRIDE) * IO::BYTES, IO::pack(f));
         }
     }
@@ -323,7 +349,7 @@ __device__ __forceinline__ void wave_row(const FwdArgs& a, uint32_t plane, int r
                                      : in;
     const int hv = sp.hv;
     with_live_slots<NV>((nin + hv + kWave - 1) / kWave, [&]<int NA>() {
-        RowPart<IO, NA, kWave, MK> p;
+        RowPart<IO, NA, kWave, MK, NV * IO::VEC >= kLeanElems> p;
         p.load(in, min, lane, hv, k);
         write_zero_slots<IO, NA, NV, kWave, SP>(out, lane);
         p.compute(lane, hv, k, a.k);
@@ -385,7 +411,7 @@ __device__ __forceinline__ void block_row(const FwdArgs& a, uint32_t plane, int 
                                      : in;
     const int hv = sp.hv;
     with_live_slots<NV>((nin + hv + T - 1) / T, [&]<int NA>() {
-        RowPart<IO, NA, T, MK> p;
+        RowPart<IO, NA, T, MK, NV * IO::VEC >= kLeanElems> p;
         p.load(in, min, t, hv, k);
         write_zero_slots<IO, NA, NV, T, SP>(out, t);
         p.compute(t, hv, k, a.k);

@@ -70,7 +70,8 @@ int64_t line_slack(bool lines, int64_t row_bytes, const void* out) {
 // may write for its predecessor (line_slack).
 //   auto:   rows up to 256 slots -> one wavefront per row (NV <= 4); longer rows -> W
 //           wavefronts per row with NV = 4 (the stores of each instruction then cover
-//           W KB of the row); W = 16 and NV up to 16 beyond that; the stream path last.
+//           W KB of the row); W = 16 and NV up to kAutoMaxNV beyond that; the stream path
+//           last.
 //   forced: the named path if it can hold the row.
 int make_plan(int64_t S, int dtype, bool wide, int64_t slack, int path, Plan* p) {
     const int64_t vec = wide ? 16 / esize_of(dtype) : 1;
@@ -78,7 +79,7 @@ int make_plan(int64_t S, int dtype, bool wide, int64_t slack, int path, Plan* p)
     p->wide = wide;
     if (path == GTMS_PATH_AUTO) {
         if (slots <= kWave * kAutoNV) path = GTMS_PATH_WAVE;
-        else if (slots <= int64_t(kWave) * kMaxW * kMaxNV) path = GTMS_PATH_BLOCK;
+        else if (slots <= int64_t(kWave) * kMaxW * kAutoMaxNV) path = GTMS_PATH_BLOCK;
         else path = GTMS_PATH_STREAM;
     }
     p->path = path;

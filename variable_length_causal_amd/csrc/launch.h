@@ -13,6 +13,13 @@ namespace gtms {
 
 constexpr int kMaxNV = 16;      // register-held vectors per lane
 constexpr int kAutoNV = 4;      // vectors per lane the automatic choice aims for
+// Vectors per lane the automatic choice takes at most on the block path; longer rows go to
+// the stream path. Measured on MI355X against forced paths: at NV = 8 the block kernels beat
+// the stream kernels (bfloat16 rows of 65536: forward 5930 vs 4979 GB/s, backward 6169 vs
+// 4953, explicit-mask backward 5332 vs 4044); at NV = 16 the row no longer fits in the 128
+// registers a lane of a 16-wavefront workgroup has, and the spilling kernels run 1.0-3.8x
+// slower than the stream kernels (bfloat16 rows of 98304, binary32 rows of 49152).
+constexpr int kAutoMaxNV = 8;
 constexpr int kWaveWPB = 4;     // wavefronts per workgroup on the wave path
 constexpr int kMaxW = 16;       // wavefronts per workgroup on the block path, at most
 constexpr int kStreamW = 8;     // wavefronts per workgroup on the stream path

@@ -63,6 +63,10 @@ WORKLOADS = {
     "skewed_bf16_8x32x8192": Workload("skewed_bf16_8x32x8192", 8, 32, 8192, BF16, 1.0, 0.125,
                                       fixed_lens=(8192, 6000, 4096, 2048, 1024, 512, 128, 1),
                                       x_seed=1005, len_seed=2005),
+    # rows of 128 KB (65536 bfloat16): the block path at its widest automatic layout, 16
+    # wavefronts of eight 16-byte vectors per lane; 34 GB per tensor
+    "long_bf16_2x2x65536": Workload("long_bf16_2x2x65536", 2, 2, 65536, BF16, 1.0, 0.125,
+                                    fixed_lens=(65536, 40000), x_seed=1006, len_seed=2006),
 }
 
 
