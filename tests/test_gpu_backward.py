@@ -148,13 +148,14 @@ def test_backward_in_place_and_poison():
 
 
 def test_backward_full_readme_shape_sampled():
-    """The binary32 3 x 64 x 1000 workload at full size: y drawn uniform in [0, 1) (the
-    backward is defined for any y), dy normal; sampled rows against the oracle."""
+    """The binary32 3 x 64 x 1000 workload at full size: y drawn uniform in [0, 2/S) (the
+    backward is defined for any y; rows summing to about 1, like the forward's outputs the
+    error bound is derived for), dy normal; sampled rows against the oracle."""
     w = workloads.WORKLOADS["readme_f32_3x64x1000"]
     lens = workloads.seq_lens(w)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(4242)
-    y = torch.rand(w.shape, generator=gen, device="cuda")
+    y = torch.rand(w.shape, generator=gen, device="cuda").mul_(2.0 / w.S)
     dy = workloads.scores_device(w.shape, w.dtype, 1.0, 4243)
     sl = torch.as_tensor(lens).cuda()
     dx = g.backward(y, dy, sl, w.scale)
