@@ -138,8 +138,49 @@ def bench_attention(args):
                      "frac": round(achieved / MFMA16_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(f"{w.name}:attention")},
         "cpu_baseline": None,
+        "device": device_info(),
     }
     print(json.dumps(out), flush=True)
+
+
+# hipDeviceAttribute_t ordinals (hip/hip_runtime_api.h, ROCm 7)
+_HIP_ATTR_MEMORY_BUS_WIDTH, _HIP_ATTR_MEMORY_CLOCK_RATE, _HIP_ATTR_MULTIPROCESSOR_COUNT = 59, 60, 63
+
+
+def device_info() -> dict:
+    """What the runtime reports about GPU 0: name, compute units, and the HBM interface (memory
+    clock in kHz, bus width in bits). The roofline's peak stays AMD's published 8 TB/s; these
+    are context. The attribute ordinals are trusted only if the compute-unit count they give
+    matches torch's."""
+    import ctypes
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    info = {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count,
+            "hbm_peak_published_gbs": HBM_PEAK_GBS}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return info
+    v = ctypes.c_int()
+
+    def attr(code):
+        return v.value if hip.hipDeviceGetAttribute(ctypes.byref(v), code, 0) == 0 else None
+    if attr(_HIP_ATTR_MULTIPROCESSOR_COUNT) == props.multi_processor_count:
+        info["hbm_clock_khz_reported"] = attr(_HIP_ATTR_MEMORY_CLOCK_RATE)
+        info["hbm_bus_bits_reported"] = attr(_HIP_ATTR_MEMORY_BUS_WIDTH)
+    return info
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def kernel_sources_hash() -> str:
@@ -193,6 +234,7 @@ def cpu_baseline(x_dev, lens, w: workloads.Workload, budget_s: float):
         "sample": f"{what} ({w.B * k} of {w.B * w.M} planes, {nbytes / 1e6:.1f} MB "
                   f"algorithmic) of the same seeded input, fp64 C oracle, one thread, "
                   f"{dt:.2f} s",
+        "cpu": cpu_model(),
     }
 
 
@@ -372,6 +414,7 @@ def main():
             "traffic": traffic,
         },
         "cpu_baseline": None,
+        "device": device_info(),
     }
     # the CPU oracle runs whole planes; planes beyond 2^26 elements (the 65536-wide rows) would
     # take minutes and tens of GB of host memory, so their lines carry no baseline

@@ -85,6 +85,36 @@ def test_attention_scales_and_long_rows():
     run_case(2, 1, 200, 64, workloads.F16, [200, 150], 2.0, seed=7)
 
 
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DNAME[d])
+@pytest.mark.parametrize("D", [64, 128])
+def test_attention_rising_scores(dtype, D):
+    """Scores that rise along the keys, so that a row's maximum keeps moving up as the key
+    blocks go by: by about 4 per 64 keys in the log2 domain (the kernel's running reference
+    sometimes moves, probabilities reach 2^8) and by about 16 (it moves every block).
+    Query dimension 0 is 1 and key dimension 0 carries the ramp; the other dimensions are
+    small noise."""
+    S, lens, scale = 640, [640, 300], 0.125
+    for rise in (4.0, 16.0):
+        shape = (2, 1, S, D)
+        q, k, v = (workloads.scores_cpu(shape, workloads.F32, 1.0, 90 + i) for i in range(3))
+        q.mul_(0.05)
+        k.mul_(0.05)
+        q[..., 0] = 1.0
+        k[..., 0] = torch.arange(S, dtype=torch.float32) * (rise / 64.0 / (scale * np.log2(np.e)))
+        q, k, v = (t.to(workloads.torch_dtype(dtype)) for t in (q, k, v))
+        qs, ks, vs = (workloads.to_storage(t) for t in (q, k, v))
+        ref = oracle.attention_f64(qs, ks, vs, lens, scale, dtype)
+        print(f"attention rising scores D={D} {DNAME[dtype]} rise={rise}", flush=True)
+        o = g.attention(q.cuda(), k.cuda(), v.cuda(),
+                        torch.as_tensor(np.asarray(lens, np.int32)).cuda(), scale)
+        torch.cuda.synchronize()
+        o_st = workloads.to_storage(o.cpu())
+        vf = to_f64(vs, dtype)
+        for b in range(2):
+            check_rows(o_st[b, 0], ref[b, 0], prefix_vmax(vf[b, 0]), [lens[b]] * S, range(S), S,
+                       dtype, f"rising {rise} D={D} {DNAME[dtype]} b={b}")
+
+
 def test_attention_ignores_padding():
     """Queries of padded rows and keys/values at or past the length change no bit."""
     B, M, S, D = 3, 2, 260, 64

@@ -45,6 +45,10 @@ struct AttnArgs {
 };
 
 constexpr int kAttnRows = 128;  // query rows per workgroup (4 wavefronts x 32)
+// The accumulators stay scaled to a row's reference max m until a block's max exceeds m by
+// more than this (log2 domain): probabilities then stay below 2^8, and the rescale runs only
+// on the few blocks that raise some row's max that far.
+constexpr float kAttnSlack = 8.0f;
 // keys per block: 64 for head size 64, 32 for 128 (keeps two workgroups' registers per SIMD)
 template <int D> constexpr int kAttnKeys = D <= 64 ? 64 : 32;
 
@@ -221,11 +225,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3
             for (int e = 0; e < 16; ++e) mb = fmaxf(mb, s[st][e]);
         }
         mb = fmaxf(mb, swap_halves(mb));
-        // running max in the log2 domain: m = max over kept keys of s * k2
-        const float m_new = fmaxf(m_run, mb == -INFINITY ? -INFINITY : mb * k2);
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_use);
-        m_run = m_new;
+        // Reference max in the log2 domain. It moves to the running max m' = max over kept
+        // keys of s * k2 only when some row of the wavefront gains more than kAttnSlack
+        // (a wave-uniform branch); the sums are then rescaled by 2^(m - m'). Softmax does
+        // not depend on the reference, so this changes rounding only; every probability
+        // stays below 2^kAttnSlack.
+        const float mk = mb == -INFINITY ? -INFINITY : mb * k2;
+        if (__builtin_amdgcn_ballot_w64(mk > m_run + kAttnSlack) != 0) {
+            const float m_new = fmaxf(m_run, mk);
+            const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_part *= alpha;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[t] *= alpha;
+        }
+        const float m_use = m_run == -INFINITY ? 0.0f : m_run;
         // probabilities, rounded to the element type for the second product
         vec8 p[2 * NS];
         float ps = 0.0f;
@@ -238,11 +252,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3
                 p[2 * st + e / 8][e % 8] = (elem_t)pe;
             }
         }
-        // rescale the running sums (alpha = 1 where the row's max did not move); done in
-        // place every block, which keeps the accumulators in the same registers
-        l_part = l_part * alpha + ps;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] *= alpha;
+        l_part += ps;
         // O^T[d][row] += V^T[d][keys] P^T[keys][row]; vector 2*st + h covers the lane's keys
         // kb + 32*st + 16h + 8*(j/4) + 4*g + j%4, j = 0..7
 #pragma unroll
