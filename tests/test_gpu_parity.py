@@ -176,6 +176,32 @@ def test_options_give_identical_bits():
                 assert np.array_equal(base, other), (DNAME[dtype], S, path, flags)
 
 
+def test_empty_inputs_are_no_ops():
+    """Zero batches, heads or rows: every entry point returns an empty result and launches
+    nothing that touches memory."""
+    for dtype in DTYPES:
+        tdt = workloads.torch_dtype(dtype)
+        for shape in ((0, 2, 5, 5), (2, 0, 5, 5), (2, 2, 0, 0)):
+            B = shape[0]
+            x = torch.zeros(shape, dtype=tdt, device="cuda")
+            sl = torch.full((B,), 3, dtype=torch.int32, device="cuda")
+            mask = torch.ones((1, 1, shape[2], shape[3]), dtype=torch.uint8, device="cuda")
+            outs = [g.forward(x, sl, 1.0), g.backward(x, x.clone(), sl, 1.0),
+                    g.forward_band(x, sl, -2, 0, 1.0), g.backward_band(x, x.clone(), sl, -2, 0),
+                    g.forward_masked(x, mask, sl, 1.0), g.backward_masked(x, x.clone(), mask, sl)]
+            torch.cuda.synchronize()
+            for o in outs:
+                assert tuple(o.shape) == shape and o.numel() == 0
+    for dtype in (workloads.F16, workloads.BF16):
+        tdt = workloads.torch_dtype(dtype)
+        for shape in ((0, 2, 8, 64), (2, 0, 8, 64), (2, 2, 0, 64)):
+            q = torch.zeros(shape, dtype=tdt, device="cuda")
+            sl = torch.full((shape[0],), 3, dtype=torch.int32, device="cuda")
+            o = g.attention(q, q.clone(), q.clone(), sl)
+            torch.cuda.synchronize()
+            assert tuple(o.shape) == shape and o.numel() == 0
+
+
 def test_in_place_and_repeat_determinism():
     for dtype in DTYPES:
         S = 513
