@@ -41,10 +41,16 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MFMA16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix-core peak, published
 METRIC = "ms and effective HBM GB/s (% of peak) for [B,M,S,S] masked softmax"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "variable_length_causal_amd", "csrc", f)
-                  for f in ("device_common.h", "forward_kernels.h", "backward_kernels.h",
-                            "gtms_api.hip", "launch.h", "launch_kind.hip",
-                            "attention_kernels.h", "launch_attention.hip")]
+# the sources each kernel family is built from; a traffic figure is valid while they are
+# unchanged
+KERNEL_SOURCES = {
+    family: [os.path.join(ROOT, "variable_length_causal_amd", "csrc", f) for f in files]
+    for family, files in (
+        ("softmax", ("device_common.h", "forward_kernels.h", "backward_kernels.h",
+                     "gtms_api.hip", "launch.h", "launch_kind.hip")),
+        ("attention", ("device_common.h", "attention_kernels.h", "gtms_api.hip", "launch.h",
+                       "launch_attention.hip")))
+}
 
 
 def algorithmic_bytes(w: workloads.Workload, lens, op: str = "forward") -> int:
@@ -183,9 +189,9 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def kernel_sources_hash() -> str:
+def kernel_sources_hash(family: str = "softmax") -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[family]:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -200,7 +206,8 @@ def measured_traffic(key: str):
     except (OSError, ValueError):
         return None
     ent = data.get(key)
-    if not ent or ent.get("kernel_sources_sha256") != kernel_sources_hash():
+    family = "attention" if key.endswith(":attention") else "softmax"
+    if not ent or ent.get("kernel_sources_sha256") != kernel_sources_hash(family):
         return None
     return ent.get("hbm_bytes_per_launch")
 
