@@ -8,10 +8,11 @@
 // reach the output). The kept set follows the mask kind MK of the forward kernels. Arithmetic is fp32; results are rounded to nearest-even into the
 // element type.
 //
-// Memory: reads the kept intervals of y and g (for the tril mask, two triangles), writes
-// every row of dx in full. The layout, buffer-resource range checks, non-temporal stores,
-// live-slot specialisation and line ownership are those of the forward kernels; the
-// reduction is a plain sum (wave DPP + readlane, then LDS across the waves of a workgroup).
+// Memory: reads the kept intervals of y and g (for the tril mask, two triangles), with
+// non-temporal loads where the read is the last; writes every row of dx in full. The layout,
+// buffer-resource range checks, non-temporal stores, live-slot specialisation and line
+// ownership are those of the forward kernels; the reduction is a plain sum (wave DPP +
+// readlane, then LDS across the waves of a workgroup).
 #pragma once
 
 #include "forward_kernels.h"
@@ -53,8 +54,8 @@ struct GradPart {
         for (int j = 0; j < NA; ++j) {
             const int v = t + j * STRIDE - hv;
             const int off = v < v0 ? kOutOfRange : v * IO::BYTES;
-            ry[j] = IO::template load<kPolicyDefault>(iny, off);
-            rg[j] = IO::template load<kPolicyDefault>(ing, off);
+            ry[j] = IO::template load<kPolicyReadOnce>(iny, off);
+            rg[j] = IO::template load<kPolicyReadOnce>(ing, off);
             if constexpr (MK == MK_MASK) mk[j] = MIO::load(min, v < v0 ? kOutOfRange : v * IO::VEC);
         }
     }
@@ -241,8 +242,8 @@ __device__ __forceinline__ void bwd_stream_row(const FwdArgs& a, uint32_t plane,
     for (int w = 0; w < W; ++w) D += pd[w];
     for (int v = v0 + t; v < nin; v += T) {
         float fy[VEC], fg[VEC], o[VEC];
-        IO::unpack(IO::template load<kPolicyDefault>(in.y, v * IO::BYTES), fy);
-        IO::unpack(IO::template load<kPolicyDefault>(in.g, v * IO::BYTES), fg);
+        IO::unpack(IO::template load<kPolicyReadOnce>(in.y, v * IO::BYTES), fy);
+        IO::unpack(IO::template load<kPolicyReadOnce>(in.g, v * IO::BYTES), fg);
         typename MIO::raw_t mb{};
         if constexpr (MK == MK_MASK) mb = MIO::load(in.m, v * VEC);
 #pragma unroll

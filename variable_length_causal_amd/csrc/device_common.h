@@ -28,9 +28,14 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kWave = 64;
 constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, blocks dealt round-robin
 
-// Cache-policy bits of a buffer access on gfx950: 0 = default, 2 = non-temporal (nt).
+// Cache-policy bits of a buffer access on gfx950: SC0 = 1, NT = 2 (non-temporal), SC1 = 16.
 constexpr int kPolicyDefault = 0;
-constexpr int kPolicyStream = 2;
+// Output stores (written once, never read back by the kernel): non-temporal at device scope.
+// Measured against NT alone on MI355X: forward +0.4% to +5%, backward +1% to +3%.
+constexpr int kPolicyStream = 2 | 16;
+// Loads of data used once (the backward's y and dy): non-temporal. Backward +2.5% to +5.7%;
+// in the forward they gained nothing.
+constexpr int kPolicyReadOnce = 2;
 
 // Raw buffer resource over [base, base + bytes): stride 0, 32-bit data format word.
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
