@@ -113,7 +113,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3
         for (int i = tid; i < (z1 - z0) * CPR; i += 256) {
             const int r = z0 + i / CPR, c = (i % CPR) * 8;
             __builtin_amdgcn_raw_buffer_store_b128(u32x4{0, 0, 0, 0}, out, (r * D + c) * 2, 0,
-                                                   kPolicyStream);
+                                                   kPolicyNt);
         }
     }
     if (q0 >= L) return;
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3
                 for (int i = 0; i < 4; ++i) o4[i] = (elem_t)(acc[t][4 * q + i] * inv);
                 const int d = 32 * t + 8 * q + 4 * g;
                 __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o4), out,
-                                                      (row * D + d) * 2, 0, kPolicyStream);
+                                                      (row * D + d) * 2, 0, kPolicyNt);
             }
         }
     }
