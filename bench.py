@@ -270,7 +270,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
-              "(the operation shards by planes with no communication; see the design notes)",
+              "(the operation shards by planes with no communication)",
               file=sys.stderr)
         sys.exit(2)
 

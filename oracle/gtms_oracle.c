@@ -24,7 +24,7 @@
  * The scale factor multiplies the scores before the softmax, as in the page
  * "优化ScaledMaskSoftmax算子" (ScaledMaskSoftmax article), sections 2.1 and 4.1.
  *
- * Readings where the pages are silent (each is listed with its reason in the design notes):
+ * Readings where the pages are silent:
  *   - seq_lens values are clamped to [0, S] (the listing's predicate tolerates any value);
  *   - results are rounded to nearest, ties to even, into the element type;
  *   - a zero is +0.0;

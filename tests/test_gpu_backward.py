@@ -3,7 +3,7 @@
 The forward output y and the upstream gradient dy are inputs of both sides: y comes from the
 oracle's rounded forward (small shapes) or a seeded uniform draw (full shapes), never from
 the GPU path. Masked elements of dx must be +0 bit for bit. Kept elements must satisfy, per
-element, the bound derived from the fp32 arithmetic (backward tolerance):
+element, the bound derived from the fp32 arithmetic:
     |dx_gpu - dx_ref| <= u * |dx_ref| + 1e-5 * scale * y_c * max_k |dy_k|
 with u = 2^-21 (binary32), 2^-10 (binary16), 2^-7 (bfloat16): the output rounding plus a
 few fp32 roundings, and the error of the fp32 dot product D (at most a few hundred terms
