@@ -269,7 +269,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the operation shards by planes with no communication)",
               file=sys.stderr)
         sys.exit(2)
