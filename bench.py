@@ -89,6 +89,31 @@ def attention_flops(w: workloads.AttnWorkload, lens) -> int:
     return 4 * w.D * pairs
 
 
+def plain_ceilings(xs, ys, n, stream, tensor_bytes):
+    """Same-run rates of torch's own plain kernels on tensors of the workload's size, as
+    context for the roofline fraction: a fill (stores only) and a copy (half reads). Each
+    is timed like the step, n back-to-back launches between two events on the stream."""
+    import torch
+    out = {}
+    for name, nbytes, op in (
+            ("plain_fill_gbs", tensor_bytes, lambda i: ys[i % len(ys)].fill_(1.0)),
+            ("plain_copy_gbs", 2 * tensor_bytes,
+             lambda i: ys[i % len(ys)].copy_(xs[(i + 1) % len(xs)]))):
+        for i in range(3):
+            op(i)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(n):
+            op(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        out[name] = round(nbytes / (a.elapsed_time(b) / n * 1e-3) / 1e9, 1)
+    out["what"] = ("torch fill_ and copy_ of one tensor of the workload's size, same GPU and "
+                   "run; bytes = stores (fill), reads + stores (copy)")
+    return out
+
+
 def bench_attention(args):
     import torch
     import variable_length_causal_amd as g
@@ -144,6 +169,7 @@ def bench_attention(args):
                      "frac": round(achieved / MFMA16_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(f"{w.name}:attention")},
         "cpu_baseline": None,
+        "context": ceilings,
         "device": device_info(),
     }
     print(json.dumps(out), flush=True)
@@ -374,6 +400,8 @@ def main():
     torch.cuda.synchronize()
     kernel_ms = [a.elapsed_time(b) for a, b in ev]
 
+    ceilings = plain_ceilings(xs, ys, min(args.steps, 50), stream, tensor_bytes)
+
     if args.copy_calibration:  # plain copy of a known size, outside the timed region
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
         dst = torch.empty_like(src)
@@ -421,6 +449,7 @@ def main():
             "traffic": traffic,
         },
         "cpu_baseline": None,
+        "context": ceilings,
         "device": device_info(),
     }
     # the CPU oracle runs whole planes; planes beyond 2^26 elements (the 65536-wide rows) would
