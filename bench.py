@@ -169,7 +169,6 @@ def bench_attention(args):
                      "frac": round(achieved / MFMA16_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(f"{w.name}:attention")},
         "cpu_baseline": None,
-        "context": ceilings,
         "device": device_info(),
     }
     print(json.dumps(out), flush=True)
