@@ -2,6 +2,8 @@
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -78,3 +80,57 @@ def path_ok(path, S, dtype, aligned=True):
     vec = 16 // esize(dtype) if wide else 1
     slack = (128 - math.gcd(row_bytes, 128)) // 16 if wide and row_bytes >= 128 else 0
     return -(-S // vec) + slack <= 64 * 16 * (16 if path == "block" else 1)
+
+
+def host_threads() -> int:
+    """Host threads for oracle work: the CPUs this process may use, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def check_planes_against_oracle(x_dev, y_dev, lens, scale: float, dtype: int,
+                                tol: float | None = None, chunk_bytes: int = 4 << 30) -> float:
+    """Every element of a [B, M, S, S] result on the device against the oracle's fp64 result:
+    masked elements +0 bit for bit, kept elements finite and within the tolerance. Planes are
+    copied to the host in chunks of at most chunk_bytes (input and output) and checked one
+    oracle call per plane on host threads (ctypes releases the GIL during the call). Returns
+    the max abs error on kept elements."""
+    import oracle
+
+    tol = TOL[dtype] if tol is None else tol
+    B, M, S, _ = y_dev.shape
+    es = esize(dtype)
+    xf = x_dev.reshape(B * M, S, S)
+    yf = y_dev.reshape(B * M, S, S)
+    keeps = {}
+    for b in range(B):
+        L = min(max(int(lens[b]), 0), S)
+        if L not in keeps:
+            keeps[L] = kept_mask(S, L)
+    per_chunk = max(1, chunk_bytes // (2 * S * S * es))
+    worst = 0.0
+    with ThreadPoolExecutor(max_workers=host_threads()) as pool:
+        for p0 in range(0, B * M, per_chunk):
+            p1 = min(B * M, p0 + per_chunk)
+            xs = workloads.to_storage(xf[p0:p1].cpu())
+            ys = workloads.to_storage(yf[p0:p1].cpu())
+
+            def one(i, xs=xs, ys=ys, p0=p0):
+                p = p0 + i
+                b = p // M
+                L = min(max(int(lens[b]), 0), S)
+                keep = keeps[L]
+                ref = oracle.softmax_f64(xs[i:i + 1][None], lens[b:b + 1], scale, dtype)[0, 0]
+                assert not bits(ys[i])[~keep].any(), f"nonzero bits in masked region of plane {p}"
+                got = to_f64(ys[i][keep], dtype)
+                assert np.all(np.isfinite(got)), f"non-finite kept output in plane {p}"
+                e = float(np.max(np.abs(got - ref[keep]))) if got.size else 0.0
+                assert e <= tol, f"plane {p} (b={b}): max error {e:.3g} > {tol:.3g}"
+                return e
+
+            worst = max([worst] + list(pool.map(one, range(p1 - p0))))
+            del xs, ys
+    return worst

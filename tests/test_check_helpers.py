@@ -1,0 +1,43 @@
+"""The every-plane parity checker of the GPU tests, run on host tensors: it accepts the
+oracle's own rounded output and rejects a planted error in a kept element, a nonzero bit in
+the masked region and a non-finite kept value."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gtms_check import TOL, check_planes_against_oracle
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.mark.parametrize("dtype", [workloads.F32, workloads.F16, workloads.BF16])
+def test_every_plane_checker(dtype):
+    lens = np.asarray([5, 0, 37, 41], dtype=np.int32)
+    x = workloads.scores_cpu((4, 3, 40, 40), dtype, 1.0, seed=42)
+    y = oracle.softmax(workloads.to_storage(x), lens, 0.7, dtype)
+    y_t = workloads.from_storage(y, dtype)
+    # a chunk of 5 planes: the 12 planes are checked in three chunks
+    chunk = 5 * 2 * 40 * 40 * (4 if dtype == workloads.F32 else 2)
+    assert check_planes_against_oracle(x, y_t, lens, 0.7, dtype, chunk_bytes=chunk) <= TOL[dtype]
+
+    def planted(b, m, r, c, value):
+        t = y_t.clone()
+        t[b, m, r, c] = value
+        return t
+
+    kept_val = float(y_t[2, 1, 20, 3])
+    with pytest.raises(AssertionError, match="max error"):
+        check_planes_against_oracle(x, planted(2, 1, 20, 3, kept_val + 0.05), lens, 0.7, dtype,
+                                    chunk_bytes=chunk)
+    with pytest.raises(AssertionError, match="masked region"):
+        check_planes_against_oracle(x, planted(0, 2, 4, 5, 1e-30 if dtype == workloads.F32
+                                               else 1e-3), lens, 0.7, dtype, chunk_bytes=chunk)
+    with pytest.raises(AssertionError, match="masked region"):
+        check_planes_against_oracle(x, planted(1, 0, 0, 0, -0.0), lens, 0.7, dtype,
+                                    chunk_bytes=chunk)
+    with pytest.raises(AssertionError, match="non-finite"):
+        check_planes_against_oracle(x, planted(3, 2, 39, 39, float("nan")), lens, 0.7, dtype,
+                                    chunk_bytes=chunk)
