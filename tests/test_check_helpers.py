@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import workloads
-from gtms_check import TOL, check_planes_against_oracle
+from gtms_check import TOL, check_planes_against_oracle, check_planes_backward_against_oracle
 
 torch = pytest.importorskip("torch")
 
@@ -41,3 +41,34 @@ def test_every_plane_checker(dtype):
     with pytest.raises(AssertionError, match="non-finite"):
         check_planes_against_oracle(x, planted(3, 2, 39, 39, float("nan")), lens, 0.7, dtype,
                                     chunk_bytes=chunk)
+
+
+@pytest.mark.parametrize("dtype", [workloads.F32, workloads.F16, workloads.BF16])
+def test_every_plane_backward_checker(dtype):
+    u = {workloads.F32: 2.0 ** -21, workloads.F16: 2.0 ** -10, workloads.BF16: 2.0 ** -7}[dtype]
+    tiny = {workloads.F32: 2.0 ** -150, workloads.F16: 2.0 ** -25, workloads.BF16: 2.0 ** -134}[dtype]
+    lens = np.asarray([5, 0, 37, 41], dtype=np.int32)
+    x = workloads.scores_cpu((4, 3, 40, 40), dtype, 1.0, seed=43)
+    y_st = oracle.softmax(workloads.to_storage(x), lens, 0.7, dtype)
+    dy = workloads.scores_cpu((4, 3, 40, 40), dtype, 1.0, seed=44)
+    ref = oracle.backward_f64(y_st, workloads.to_storage(dy), lens, 0.7, dtype)
+    y_t = workloads.from_storage(y_st, dtype)
+    # the oracle's backward rounded to the element type passes
+    dx = torch.as_tensor(ref).to(y_t.dtype)
+    chunk = 5 * 3 * 40 * 40 * (4 if dtype == workloads.F32 else 2)
+    check_planes_backward_against_oracle(y_t, dy, dx, lens, 0.7, dtype, u, tiny,
+                                         chunk_bytes=chunk, row_block=16)
+
+    def planted(b, m, r, c, value):
+        t = dx.clone()
+        t[b, m, r, c] = value
+        return t
+
+    with pytest.raises(AssertionError, match="beyond the bound"):
+        check_planes_backward_against_oracle(
+            y_t, dy, planted(2, 1, 20, 3, float(dx[2, 1, 20, 3]) + 0.05), lens, 0.7, dtype, u,
+            tiny, chunk_bytes=chunk, row_block=16)
+    with pytest.raises(AssertionError, match="masked region"):
+        check_planes_backward_against_oracle(
+            y_t, dy, planted(1, 0, 3, 2, -0.0), lens, 0.7, dtype, u, tiny, chunk_bytes=chunk,
+            row_block=16)

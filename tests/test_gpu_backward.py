@@ -17,7 +17,8 @@ import pytest
 
 import oracle
 import workloads
-from gtms_check import bits, kept_mask, kept_row, path_ok, to_f64
+from gtms_check import (bits, check_planes_backward_against_oracle, kept_mask, kept_row,
+                        path_ok, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -147,32 +148,26 @@ def test_backward_in_place_and_poison():
         assert np.array_equal(bits(workloads.to_storage(dxp.cpu())), bits(dx_st))
 
 
-def test_backward_full_readme_shape_sampled():
-    """The binary32 3 x 64 x 1000 workload at full size: y drawn uniform in [0, 2/S) (the
-    backward is defined for any y; rows summing to about 1, like the forward's outputs the
-    error bound is derived for), dy normal; sampled rows against the oracle."""
-    w = workloads.WORKLOADS["readme_f32_3x64x1000"]
+@pytest.mark.parametrize("name", ["readme_f32_3x64x1000", "readme_f32_12x64x1000",
+                                  "scaled_f16_32x1x4096", "skewed_bf16_8x32x8192"])
+def test_backward_full_workload(name):
+    """A benchmark workload at full size through the default entry point: y drawn uniform in
+    [0, 2/S) (the backward is defined for any y; rows summing to about 1, like the forward's
+    outputs the error bound is derived for), dy normal; every element of every plane against
+    the oracle's backward."""
+    w = workloads.WORKLOADS[name]
     lens = workloads.seq_lens(w)
+    print(f"backward full workload {name} lens={list(lens)}", flush=True)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(4242)
-    y = torch.rand(w.shape, generator=gen, device="cuda").mul_(2.0 / w.S)
+    y = torch.rand(w.shape, generator=gen, device="cuda",
+                   dtype=workloads.torch_dtype(w.dtype)).mul_(2.0 / w.S)
     dy = workloads.scores_device(w.shape, w.dtype, 1.0, 4243)
     sl = torch.as_tensor(lens).cuda()
     dx = g.backward(y, dy, sl, w.scale)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(5)
-    rows = [(int(rng.integers(w.B)), int(rng.integers(w.M)), int(rng.integers(w.S)))
-            for _ in range(600)]
-    rows += [(b, 0, r) for b in range(w.B) for r in (0, int(lens[b]) - 1, int(lens[b]), w.S - 1)]
-    ys = torch.stack([y[b, m, r] for b, m, r in rows]).cpu()
-    gs = torch.stack([dy[b, m, r] for b, m, r in rows]).cpu()
-    ds = torch.stack([dx[b, m, r] for b, m, r in rows]).cpu()
-    y_st, g_st = workloads.to_storage(ys), workloads.to_storage(gs)
-    ref = np.empty((len(rows), w.S))
-    for i, (b, m, r) in enumerate(rows):   # one [1, 1, S, S] plane holding only this row
-        yy = np.zeros((1, 1, w.S, w.S), dtype=np.float32)
-        gg = np.zeros((1, 1, w.S, w.S), dtype=np.float32)
-        yy[0, 0, r], gg[0, 0, r] = y_st[i], g_st[i]
-        ref[i] = oracle.backward_f64(yy, gg, [lens[b]], w.scale, w.dtype)[0, 0, r]
-    check_rows(workloads.to_storage(ds), ref, y_st, g_st, [lens[b] for b, _, _ in rows],
-               [r for _, _, r in rows], w.scale, w.dtype)
+    worst = check_planes_backward_against_oracle(y, dy, dx, lens, w.scale, w.dtype, U[w.dtype],
+                                                 TINY[w.dtype])
+    print(f"{name}: every plane of the backward checked, worst error {worst:.3g}", flush=True)
+    del y, dy, dx
+    torch.cuda.empty_cache()
