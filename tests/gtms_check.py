@@ -92,12 +92,17 @@ def host_threads() -> int:
 
 
 def check_planes_against_oracle(x_dev, y_dev, lens, scale: float, dtype: int,
-                                tol: float | None = None, chunk_bytes: int = 4 << 30) -> float:
+                                tol: float | None = None, chunk_bytes: int = 4 << 30,
+                                plane_ref=None) -> float:
     """Every element of a [B, M, S, S] result on the device against the oracle's fp64 result:
     masked elements +0 bit for bit, kept elements finite and within the tolerance. Planes are
     copied to the host in chunks of at most chunk_bytes (input and output) and checked one
     oracle call per plane on host threads (ctypes releases the GIL during the call). Returns
-    the max abs error on kept elements."""
+    the max abs error on kept elements.
+
+    plane_ref(x_plane, p) -> (ref [S, S] fp64, keep [S, S] bool) gives the reference and the
+    kept set of flat plane p = b * M + m from its raw input [1, 1, S, S]; by default the
+    grouped tril mask with the lengths `lens` (the mask variants pass their own)."""
     import oracle
 
     tol = TOL[dtype] if tol is None else tol
@@ -105,11 +110,18 @@ def check_planes_against_oracle(x_dev, y_dev, lens, scale: float, dtype: int,
     es = esize(dtype)
     xf = x_dev.reshape(B * M, S, S)
     yf = y_dev.reshape(B * M, S, S)
-    keeps = {}
-    for b in range(B):
-        L = min(max(int(lens[b]), 0), S)
-        if L not in keeps:
-            keeps[L] = kept_mask(S, L)
+    if plane_ref is None:
+        keeps = {}
+        for b in range(B):
+            L = min(max(int(lens[b]), 0), S)
+            if L not in keeps:
+                keeps[L] = kept_mask(S, L)
+
+        def plane_ref(x_plane, p):
+            b = p // M
+            ref = oracle.softmax_f64(x_plane, lens[b:b + 1], scale, dtype)[0, 0]
+            return ref, keeps[min(max(int(lens[b]), 0), S)]
+
     per_chunk = max(1, chunk_bytes // (2 * S * S * es))
     worst = 0.0
     with ThreadPoolExecutor(max_workers=host_threads()) as pool:
@@ -120,15 +132,12 @@ def check_planes_against_oracle(x_dev, y_dev, lens, scale: float, dtype: int,
 
             def one(i, xs=xs, ys=ys, p0=p0):
                 p = p0 + i
-                b = p // M
-                L = min(max(int(lens[b]), 0), S)
-                keep = keeps[L]
-                ref = oracle.softmax_f64(xs[i:i + 1][None], lens[b:b + 1], scale, dtype)[0, 0]
+                ref, keep = plane_ref(xs[i:i + 1][None], p)
                 assert not bits(ys[i])[~keep].any(), f"nonzero bits in masked region of plane {p}"
                 got = to_f64(ys[i][keep], dtype)
                 assert np.all(np.isfinite(got)), f"non-finite kept output in plane {p}"
                 e = float(np.max(np.abs(got - ref[keep]))) if got.size else 0.0
-                assert e <= tol, f"plane {p} (b={b}): max error {e:.3g} > {tol:.3g}"
+                assert e <= tol, f"plane {p}: max error {e:.3g} > {tol:.3g}"
                 return e
 
             worst = max([worst] + list(pool.map(one, range(p1 - p0))))

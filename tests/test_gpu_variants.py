@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 import workloads
-from gtms_check import TOL, bits, kept_row, path_ok, to_f64
+from gtms_check import TOL, bits, check_planes_against_oracle, kept_row, path_ok, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -340,23 +340,10 @@ def grad_check_rows(st, ref, y_st, dy_st, keep, scale, dtype, tag):
     assert np.all(err[keep] <= bound[keep]), f"{tag}: {float(np.max((err - bound)[keep]))}"
 
 
-def sampled_rows(x_dev, y_dev, rows, ref_row, dtype):
-    """Compare sampled rows (b, m, r) of a full-size launch with the oracle on one-row
-    planes: ref_row(b, r, row_storage) returns the fp64 reference row and its kept flags."""
-    xs = workloads.to_storage(torch.stack([x_dev[b, m, r] for b, m, r in rows]).cpu())
-    ys = workloads.to_storage(torch.stack([y_dev[b, m, r] for b, m, r in rows]).cpu())
-    got, yb = to_f64(ys, dtype), bits(ys)
-    for i, (b, m, r) in enumerate(rows):
-        ref, keep = ref_row(b, r, xs[i])
-        assert not yb[i][~keep].any(), (b, m, r)
-        if keep.any():
-            assert float(np.max(np.abs(got[i][keep] - ref[keep]))) <= TOL[dtype], (b, m, r)
-
-
-def test_full_size_window_and_key_masks_sampled():
-    """Full workload shapes: a causal window of 512 columns on binary16 32 x 1 x 4096, and
-    per-sample key masks [B, 1, 1, S] (the article's length mask) on binary32 3 x 64 x 1000."""
-    rng = np.random.default_rng(61)
+def test_full_size_window_and_key_masks():
+    """Full workload shapes, every element of every plane against the oracle: a causal window
+    of 512 columns on binary16 32 x 1 x 4096, and per-sample key masks [B, 1, 1, S] (the
+    article's length mask) on binary32 3 x 64 x 1000."""
     w = workloads.WORKLOADS["scaled_f16_32x1x4096"]
     lens = workloads.seq_lens(w)
     x = workloads.scores_device(w.shape, w.dtype, w.sigma, w.x_seed, "cuda")
@@ -364,13 +351,13 @@ def test_full_size_window_and_key_masks_sampled():
     torch.cuda.synchronize()
     S = w.S
 
-    def ref_band(b, r, row):
-        plane = np.zeros((1, 1, S, S), dtype=row.dtype)
-        plane[0, 0, r] = row
-        ref = oracle.softmax_band_f64(plane, [lens[b]], -511, 0, w.scale, w.dtype)[0, 0, r]
-        return ref, band_keep(S, lens[b], -511, 0)[r]
-    rows = [(int(rng.integers(w.B)), 0, int(rng.integers(S))) for _ in range(60)]
-    sampled_rows(x, y, rows, ref_band, w.dtype)
+    def ref_band(x_plane, p):
+        b = p // w.M
+        ref = oracle.softmax_band_f64(x_plane, lens[b:b + 1], -511, 0, w.scale, w.dtype)[0, 0]
+        return ref, band_keep(S, lens[b], -511, 0)
+    worst = check_planes_against_oracle(x, y, lens, w.scale, w.dtype, plane_ref=ref_band)
+    print(f"window tril(512) on {w.name}: every plane checked, worst error {worst:.3g}",
+          flush=True)
     del x, y
 
     w = workloads.WORKLOADS["readme_f32_3x64x1000"]
@@ -382,11 +369,9 @@ def test_full_size_window_and_key_masks_sampled():
     y = g.forward_masked(x, torch.as_tensor(key).cuda(), None, w.scale)
     torch.cuda.synchronize()
 
-    def ref_key(b, r, row):
-        plane = np.zeros((1, 1, S, S), dtype=row.dtype)
-        plane[0, 0, r] = row
-        ref = oracle.softmax_masked_f64(plane, key[b:b + 1], None, w.scale, w.dtype)[0, 0, r]
-        return ref, key[b, 0, 0].astype(bool)
-    rows = [(int(rng.integers(w.B)), int(rng.integers(w.M)), int(rng.integers(S)))
-            for _ in range(200)]
-    sampled_rows(x, y, rows, ref_key, w.dtype)
+    def ref_key(x_plane, p):
+        b = p // w.M
+        ref = oracle.softmax_masked_f64(x_plane, key[b:b + 1], None, w.scale, w.dtype)[0, 0]
+        return ref, np.broadcast_to(key[b, 0, 0].astype(bool), (S, S))
+    worst = check_planes_against_oracle(x, y, None, w.scale, w.dtype, plane_ref=ref_key)
+    print(f"key masks on {w.name}: every plane checked, worst error {worst:.3g}", flush=True)
