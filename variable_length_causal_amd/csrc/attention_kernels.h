@@ -218,20 +218,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3
                     s[st][e] = 32 * st + 8 * (e / 4) + (e & 3) <= lim ? s[st][e] : -INFINITY;
             }
         }
-        float mb = -INFINITY;
+        // this lane's half of the row: max over its 8 keys per 32-key tile
+        float mh = -INFINITY;
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) mb = fmaxf(mb, s[st][e]);
+            for (int e = 0; e < 16; ++e) mh = fmaxf(mh, s[st][e]);
         }
-        mb = fmaxf(mb, swap_halves(mb));
         // Reference max in the log2 domain. It moves to the running max m' = max over kept
         // keys of s * k2 only when some row of the wavefront gains more than kAttnSlack
         // (a wave-uniform branch); the sums are then rescaled by 2^(m - m'). Softmax does
         // not depend on the reference, so this changes rounding only; every probability
-        // stays below 2^kAttnSlack.
-        const float mk = mb == -INFINITY ? -INFINITY : mb * k2;
-        if (__builtin_amdgcn_ballot_w64(mk > m_run + kAttnSlack) != 0) {
+        // stays below 2^kAttnSlack. A row's max exceeds the bound exactly when one of its two
+        // halves does (m_run is the same on both lanes of a row, and k2 >= 0), so the
+        // wave-wide test runs on the halves and the exchange with lane l ^ 32 that gives
+        // the row max happens only inside the branch.
+        const float mkh = mh == -INFINITY ? -INFINITY : mh * k2;
+        if (__builtin_amdgcn_ballot_w64(mkh > m_run + kAttnSlack) != 0) {
+            const float mb = fmaxf(mh, swap_halves(mh));
+            const float mk = mb == -INFINITY ? -INFINITY : mb * k2;
             const float m_new = fmaxf(m_run, mk);
             const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
             m_run = m_new;
