@@ -148,6 +148,12 @@ def bench_attention(args):
     avg_kernel_ms = ev0.elapsed_time(ev1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
     achieved = flops / (avg_kernel_ms * 1e-3) / 1e12
+    if args.copy_calibration:  # plain copy of a known size, outside the timed region
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     out = {
         "metric": "TFLOP/s of the fused attention with the grouped tril mask",
         "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
@@ -171,7 +177,50 @@ def bench_attention(args):
         "cpu_baseline": None,
         "device": device_info(),
     }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_attention(qkv[0], lens, w, args.cpu_budget)
     print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_attention(qkv_dev, lens, w: workloads.AttnWorkload, budget_s: float):
+    """Time the CPU oracle's attention, as it stands, on whole heads of the same input: one
+    oracle call per head on T host threads, over the first k heads of every batch, k as many
+    as fit the time budget (wall seconds)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    T = host_threads()
+    probe_b = int(np.argmax(lens))
+    one = [workloads.to_storage(t[probe_b:probe_b + 1, :1].cpu()) for t in qkv_dev]
+    t0 = time.perf_counter()
+    oracle.attention_f64(*one, lens[probe_b:probe_b + 1], w.scale, w.dtype)
+    per_head = max(time.perf_counter() - t0, 1e-6)
+    k = int(max(1, min(w.M, budget_s * T / (per_head * w.B))))
+    qs, ks, vs = (workloads.to_storage(t[:, :k].contiguous().cpu()) for t in qkv_dev)
+    tasks = [(b, m) for b in range(w.B) for m in range(k)]
+
+    def run(task):
+        b, m = task
+        oracle.attention_f64(qs[b:b + 1, m:m + 1], ks[b:b + 1, m:m + 1], vs[b:b + 1, m:m + 1],
+                             lens[b:b + 1], w.scale, w.dtype)
+
+    with ThreadPoolExecutor(max_workers=T) as pool:
+        t0 = time.perf_counter()
+        list(pool.map(run, tasks))
+        dt = time.perf_counter() - t0
+    sub = workloads.AttnWorkload(w.name, w.B, k, w.S, w.D, w.dtype, w.len_lo, w.len_hi)
+    flops = attention_flops(sub, lens)
+    what = "all heads" if k == w.M else f"heads m < {k} of every batch"
+    return {
+        "value": round(flops / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": T,
+        "kind": "oracle",
+        "sample": f"{what} ({w.B * k} of {w.B * w.M} heads, {flops / 1e9:.2f} GFLOP) of the "
+                  f"same seeded input, fp64 C oracle (single-threaded), one call per head on "
+                  f"{T} host threads, {dt:.2f} s wall",
+        "cpu": cpu_model(),
+    }
 
 
 # hipDeviceAttribute_t ordinals (hip/hip_runtime_api.h, ROCm 7)

@@ -283,22 +283,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3
         __syncthreads();
     }
 
-    // normalise and store the rows below L (acc[t] register e: d = 32t + 8*(e/4) + 4g + e%4)
+    // Normalise and store the rows below L (acc[t] register e: d = 32t + 8*(e/4) + 4g + e%4).
+    // A lane holds 4-element pieces of its row, so stores straight from the accumulators
+    // would fill each 128-byte line in eight partial writes. Each wavefront therefore stages
+    // its 32 rows, 64 columns at a time, in the V^T buffer (free since the loop's last
+    // barrier) and reads them back as 16-byte row chunks: every store instruction then
+    // writes 8 whole rows of 64 columns. Only this wavefront touches its staging rows, so a
+    // fence (no barrier) orders its LDS writes before its reads and its reads before the next
+    // pass's writes.
+    constexpr int OP = 64 + 8;  // staging row pitch (elements)
+    static_assert(4 * 32 * OP <= 2 * D * VP, "staging area");
     const float l_row = l_part + swap_halves(l_part);
-    if (row < L) {
-        const float inv = 1.0f / l_row;
+    const float inv = row < L ? 1.0f / l_row : 0.0f;
+    elem_t* obuf = reinterpret_cast<elem_t*>(vt_lds) + wave * 32 * OP;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
+    for (int t0 = 0; t0 < NT; t0 += 2) {
+#pragma unroll
+        for (int t = t0; t < t0 + 2; ++t) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 vec4 o4;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) o4[i] = (elem_t)(acc[t][4 * q + i] * inv);
-                const int d = 32 * t + 8 * q + 4 * g;
-                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o4), out,
-                                                      (row * D + d) * 2, 0, kPolicyNt);
+                *(vec4*)&obuf[(lane & 31) * OP + 32 * (t - t0) + 8 * q + 4 * g] = o4;
             }
         }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        u32x4 val[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            val[i] = *(const u32x4*)&obuf[(8 * i + (lane >> 3)) * OP + 8 * (lane & 7)];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            // rows at or past L keep the zeros written above: their stores get an offset that
+            // the buffer range check drops
+            const int grow = row_lo + 8 * i + (lane >> 3);
+            __builtin_amdgcn_raw_buffer_store_b128(
+                val[i], out, grow < L ? (grow * D + 32 * t0 + 8 * (lane & 7)) * 2 : (int)0x80000000,
+                0, kPolicyNt);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
     }
 }
 
