@@ -42,6 +42,7 @@ struct AttnArgs {
     int S;
     int n_tiles;        // ceil(S / kAttnRows)
     float k2;           // scale * log2(e)
+    int tile_major;     // block order (see attn_fwd)
 };
 
 constexpr int kAttnRows = 128;  // query rows per workgroup (4 wavefronts x 32)
@@ -94,12 +95,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3
     __shared__ __attribute__((aligned(16))) elem_t k_lds[2][BN * KP];
     __shared__ __attribute__((aligned(16))) elem_t vt_lds[2][D * VP];
 
-    // Block order: all the tiles of one plane run on one XCD (its L2 then holds the
-    // plane's K and V once for all of them), the tiles with the most key blocks first.
+    // Block order, chosen by the host:
+    //  - tile-major: the last tile of every plane first, then the one before, and so on, so
+    //    the longest tiles start first and none waits behind whole planes. With a multiple of
+    //    8 planes, block i runs on XCD i % 8 and each plane stays on one XCD;
+    //  - plane-major: all the tiles of one plane run on one XCD, one after the other, longest
+    //    first; its L2 then holds the plane's K and V once for all of them.
+    // Tile-major re-reads a plane's K and V after a sweep over all planes, which costs HBM
+    // bandwidth once they no longer fit in the memory-side cache and the tiles run fast.
     const uint32_t nt = (uint32_t)a.n_tiles;
-    const uint32_t lb = xcd_grouped(blockIdx.x, gridDim.x, nt);
-    const uint32_t plane = lb / nt;
-    const int qt = (int)(nt - 1 - lb % nt);
+    uint32_t plane;
+    int qt;
+    if (a.tile_major) {
+        const uint32_t rank = blockIdx.x / a.n_planes;
+        plane = blockIdx.x - rank * a.n_planes;
+        qt = (int)(nt - 1 - rank);
+    } else {
+        const uint32_t lb = xcd_grouped(blockIdx.x, gridDim.x, nt);
+        plane = lb / nt;
+        qt = (int)(nt - 1 - lb % nt);
+    }
     const int q0 = qt * kAttnRows;
     const int L = clamp_len(a.seq_lens[plane / a.M], a.S);
     const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6), g = lane >> 5;
