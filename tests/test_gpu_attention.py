@@ -185,3 +185,29 @@ def test_attention_full_workload(name):
     with ThreadPoolExecutor(max_workers=host_threads()) as pool:
         worst = max(pool.map(one, [(b, m) for b in range(w.B) for m in range(w.M)]))
     print(f"{name}: every row of every head checked, worst error {worst:.3g}", flush=True)
+
+
+def test_attention_plane_major_head_size_128():
+    """bf16 [32, 8, 4096, 128]: the heads' K and V (537 MB) exceed what the tile-major block
+    order is used for, so this runs the plane-major order at head size 128. Sampled rows
+    against the oracle's one-row entry point; every padded row zero and every output
+    finite."""
+    B, M, S, D = 32, 8, 4096, 128
+    lens = workloads.seq_lens(workloads.ATTN_WORKLOADS["attn_bf16_32x8x4096_d64"])
+    q, k, v = (workloads.scores_device((B, M, S, D), workloads.BF16, 1.0, 3100 + i, "cuda")
+               for i in range(3))
+    o = g.attention(q, k, v, torch.as_tensor(lens).cuda(), 0.09)
+    torch.cuda.synchronize()
+    for b, L in enumerate(lens):
+        assert not torch.any(o[b, :, int(L):] != 0).item(), f"padded rows of batch {b}"
+        assert torch.isfinite(o[b, :, :int(L)]).all().item()
+    rng = np.random.default_rng(17)
+    for _ in range(40):
+        b, m = int(rng.integers(B)), int(rng.integers(M))
+        L = int(lens[b])
+        qs, ks, vs = (workloads.to_storage(t[b, m].cpu()) for t in (q, k, v))
+        vmax = prefix_vmax(to_f64(vs, workloads.BF16))
+        for r in {0, L - 1, int(rng.integers(L)), int(rng.integers(L))}:
+            ref = oracle.attention_row_f64(qs, ks, vs, r, L, 0.09, workloads.BF16)
+            ost = workloads.to_storage(o[b, m, r:r + 1].cpu())
+            check_rows(ost, ref[None], [vmax[r]], [L], [r], S, workloads.BF16, f"b={b} m={m}")
