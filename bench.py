@@ -148,6 +148,15 @@ def bench_attention(args):
     avg_kernel_ms = ev0.elapsed_time(ev1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
     achieved = flops / (avg_kernel_ms * 1e-3) / 1e12
+    # after the timed region: per-launch events for the spread of single launch times
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(min(args.steps, 50))]
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        step(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    kernel_ms = [a.elapsed_time(b) for a, b in ev]
     if args.copy_calibration:  # plain copy of a known size, outside the timed region
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
         dst = torch.empty_like(src)
@@ -169,7 +178,9 @@ def bench_attention(args):
         "data": "synthetic (seeded normal q, k, v generated on the device, seeded lengths)",
         "config": {"workload": w.name, "op": "attention", "B": w.B, "M": w.M, "S": w.S,
                    "D": w.D, "seq_lens": [int(v) for v in lens], "scale": w.scale,
-                   "flops_per_step": flops},
+                   "flops_per_step": flops,
+                   "kernel_ms_min": round(float(np.min(kernel_ms)), 5),
+                   "kernel_ms_median": round(float(np.median(kernel_ms)), 5)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": MFMA16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA16_PEAK_TFLOPS, 4),
