@@ -199,3 +199,38 @@ def check_planes_backward_against_oracle(y_dev, dy_dev, dx_dev, lens, scale: flo
             worst = max([worst] + list(pool.map(one, range(p1 - p0))))
             del ys, gs, ds
     return worst
+
+
+def check_rows_against_oracle(x_dev, y_dev, lens, scale: float, dtype: int,
+                              tol: float | None = None, rows_per_call: int = 1024) -> float:
+    """Every element of a [B, M, S, S] forward result on the device, for planes too large to
+    hand to the oracle whole: blocks of rows_per_call rows go to the host and through the
+    oracle's row entry point, one block per host thread. Masked elements +0 bit for bit, kept
+    elements finite and within the tolerance. Returns the max abs error on kept elements."""
+    import oracle
+
+    tol = TOL[dtype] if tol is None else tol
+    B, M, S, _ = y_dev.shape
+    col = np.arange(S)[None, :]
+    tasks = [(b, m, r0) for b in range(B) for m in range(M) for r0 in range(0, S, rows_per_call)]
+
+    def one(task):
+        b, m, r0 = task
+        r1 = min(S, r0 + rows_per_call)
+        L = min(max(int(lens[b]), 0), S)
+        xs = workloads.to_storage(x_dev[b, m, r0:r1].cpu())
+        ys = workloads.to_storage(y_dev[b, m, r0:r1].cpu())
+        r = np.arange(r0, r1)[:, None]
+        keep = (col <= r) & (r < L)
+        assert not bits(ys)[~keep].any(), f"nonzero bits in masked region of b={b} m={m} rows {r0}.."
+        if not keep.any():
+            return 0.0
+        ref = oracle.softmax_rows_f64(xs, np.arange(r0, r1), [lens[b]] * (r1 - r0), scale, dtype)
+        got = to_f64(ys[keep], dtype)
+        assert np.all(np.isfinite(got)), f"non-finite kept output in b={b} m={m} rows {r0}.."
+        e = float(np.max(np.abs(got - ref[keep])))
+        assert e <= tol, f"b={b} m={m} rows {r0}..{r1}: max error {e:.3g} > {tol:.3g}"
+        return e
+
+    with ThreadPoolExecutor(max_workers=host_threads()) as pool:
+        return max([0.0] + list(pool.map(one, tasks)))

@@ -8,7 +8,8 @@ import pytest
 
 import oracle
 import workloads
-from gtms_check import TOL, check_planes_against_oracle, check_planes_backward_against_oracle
+from gtms_check import (TOL, check_planes_against_oracle, check_planes_backward_against_oracle,
+                        check_rows_against_oracle)
 
 torch = pytest.importorskip("torch")
 
@@ -72,3 +73,19 @@ def test_every_plane_backward_checker(dtype):
         check_planes_backward_against_oracle(
             y_t, dy, planted(1, 0, 3, 2, -0.0), lens, 0.7, dtype, u, tiny, chunk_bytes=chunk,
             row_block=16)
+
+
+@pytest.mark.parametrize("dtype", [workloads.F32, workloads.BF16])
+def test_row_block_checker(dtype):
+    lens = np.asarray([5, 0, 37, 41], dtype=np.int32)
+    x = workloads.scores_cpu((4, 3, 40, 40), dtype, 1.0, seed=45)
+    y = workloads.from_storage(oracle.softmax(workloads.to_storage(x), lens, 0.7, dtype), dtype)
+    assert check_rows_against_oracle(x, y, lens, 0.7, dtype, rows_per_call=16) <= TOL[dtype]
+    bad = y.clone()
+    bad[2, 1, 33, 30] += 0.05
+    with pytest.raises(AssertionError, match="max error"):
+        check_rows_against_oracle(x, bad, lens, 0.7, dtype, rows_per_call=16)
+    bad = y.clone()
+    bad[3, 0, 12, 13] = -0.0
+    with pytest.raises(AssertionError, match="masked region"):
+        check_rows_against_oracle(x, bad, lens, 0.7, dtype, rows_per_call=16)

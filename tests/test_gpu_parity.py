@@ -4,8 +4,8 @@ Masked elements must be +0.0 bit for bit; kept elements must lie within the elem
 tolerance of the oracle's fp64 result (binary32 2e-6, binary16 2e-3, bfloat16 8e-3).
 Small shapes and the benchmark workloads at full size, launched exactly as the benchmark
 launches them, are compared element by element (the full sizes plane by plane on host
-threads); rows of 65536 and more elements are compared on sampled rows plus properties
-checked on every row (exact zeros, row sums).
+threads; rows of 65536 elements in blocks of rows through the oracle's row entry point).
+Rows longer than that, forced through each path, are compared on sampled rows.
 """
 from __future__ import annotations
 
@@ -14,8 +14,8 @@ import pytest
 
 import oracle
 import workloads
-from gtms_check import (TOL, bits, check_against_oracle, check_planes_against_oracle, kept_mask,
-                        kept_row, path_ok, to_f64)
+from gtms_check import (TOL, bits, check_against_oracle, check_planes_against_oracle,
+                        check_rows_against_oracle, kept_mask, kept_row, path_ok, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -335,8 +335,8 @@ def test_side_stream_and_graph_replay():
 
 def test_full_long_bf16_2x2x65536():
     """Rows of 65536 bfloat16 elements (the block path at eight 16-byte vectors per lane) at
-    the benchmark's size: sampled rows against the oracle, and on every row, in chunks of rows,
-    exact zeros past the kept prefix and kept rows that sum to 1."""
+    the benchmark's size: every element against the oracle, in blocks of 1024 rows through the
+    oracle's row entry point (a plane of 4.3e9 elements is too large to hand over whole)."""
     name = "long_bf16_2x2x65536"
     w = workloads.WORKLOADS[name]
     lens = workloads.seq_lens(w)
@@ -344,25 +344,7 @@ def test_full_long_bf16_2x2x65536():
     x = workloads.scores_device(w.shape, w.dtype, w.sigma, w.x_seed)
     y = g.forward(x, torch.as_tensor(lens).cuda(), w.scale)
     torch.cuda.synchronize()
-    B, M, S, _ = w.shape
-    rng = np.random.default_rng(w.x_seed)
-    rows = [(b, int(rng.integers(M)), r) for b in range(B)
-            for r in {0, int(lens[b]) - 1, min(int(lens[b]), S - 1), S - 1}]
-    rows += [(int(rng.integers(B)), int(rng.integers(M)), int(rng.integers(S))) for _ in range(60)]
-    worst = sample_rows_check(x, y, lens, w.scale, w.dtype, rows)
-    col = torch.arange(S, device="cuda")
-    for b in range(B):
-        L = int(lens[b])
-        for m in range(M):
-            for r0 in range(0, S, 2048):
-                blk = y[b, m, r0:r0 + 2048]
-                r = torch.arange(r0, r0 + blk.shape[0], device="cuda")
-                masked = (col[None, :] > r[:, None]) | (r[:, None] >= L)
-                assert not (blk.view(torch.int16)[masked] != 0).any(), (b, m, r0)
-                kept = int(max(0, min(L, r0 + blk.shape[0]) - r0))
-                if kept:
-                    sums = blk[:kept].float().sum(dim=1)
-                    assert float((sums - 1).abs().max()) <= 1.6e-2, (b, m, r0)
-    print(f"{name}: worst sampled error {worst:.3g}", flush=True)
+    worst = check_rows_against_oracle(x, y, lens, w.scale, w.dtype)
+    print(f"{name}: every element checked, worst error {worst:.3g}", flush=True)
     del x, y
     torch.cuda.empty_cache()
