@@ -234,3 +234,41 @@ def check_rows_against_oracle(x_dev, y_dev, lens, scale: float, dtype: int,
 
     with ThreadPoolExecutor(max_workers=host_threads()) as pool:
         return max([0.0] + list(pool.map(one, tasks)))
+
+
+def check_rows_backward_against_oracle(y_dev, dy_dev, dx_dev, lens, scale: float, dtype: int,
+                                       u: float, tiny: float, rows_per_call: int = 512) -> float:
+    """The backward counterpart of check_rows_against_oracle: every element of dx against the
+    oracle's backward row entry point, blocks of rows_per_call rows on host threads; masked
+    elements +0 bit for bit, kept elements finite and within
+    u * |dx_ref| + 1e-5 * |scale| * y_c * max_k |dy_k| + tiny. Returns the max abs error."""
+    import oracle
+
+    B, M, S, _ = dx_dev.shape
+    col = np.arange(S)[None, :]
+    tasks = [(b, m, r0) for b in range(B) for m in range(M) for r0 in range(0, S, rows_per_call)]
+
+    def one(task):
+        b, m, r0 = task
+        r1 = min(S, r0 + rows_per_call)
+        L = min(max(int(lens[b]), 0), S)
+        ys, gs, ds = (workloads.to_storage(t[b, m, r0:r1].cpu()) for t in (y_dev, dy_dev, dx_dev))
+        r = np.arange(r0, r1)[:, None]
+        keep = (col <= r) & (r < L)
+        assert not bits(ds)[~keep].any(), f"nonzero bits in masked region of b={b} m={m} rows {r0}.."
+        if not keep.any():
+            return 0.0
+        ref = oracle.backward_rows_f64(ys, gs, np.arange(r0, r1), [lens[b]] * (r1 - r0), scale,
+                                       dtype)
+        got = to_f64(ds, dtype)
+        yv = to_f64(ys, dtype)
+        gmax = np.where(keep, np.abs(to_f64(gs, dtype)), 0.0).max(axis=1, keepdims=True)
+        err = np.abs(got - ref)
+        bound = u * np.abs(ref) + 1e-5 * abs(scale) * yv * gmax + tiny
+        assert np.all(np.isfinite(got[keep])), f"non-finite kept output in b={b} m={m} rows {r0}.."
+        bad = keep & ~(err <= bound)
+        assert not bad.any(), f"b={b} m={m} rows {r0}..{r1}: {int(bad.sum())} kept elements beyond the bound"
+        return float(np.max(np.where(keep, err, 0.0)))
+
+    with ThreadPoolExecutor(max_workers=host_threads()) as pool:
+        return max([0.0] + list(pool.map(one, tasks)))

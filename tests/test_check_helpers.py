@@ -9,7 +9,7 @@ import pytest
 import oracle
 import workloads
 from gtms_check import (TOL, check_planes_against_oracle, check_planes_backward_against_oracle,
-                        check_rows_against_oracle)
+                        check_rows_against_oracle, check_rows_backward_against_oracle)
 
 torch = pytest.importorskip("torch")
 
@@ -89,3 +89,26 @@ def test_row_block_checker(dtype):
     bad[3, 0, 12, 13] = -0.0
     with pytest.raises(AssertionError, match="masked region"):
         check_rows_against_oracle(x, bad, lens, 0.7, dtype, rows_per_call=16)
+
+
+def test_row_block_backward_checker():
+    dtype = workloads.F16
+    u, tiny = 2.0 ** -10, 2.0 ** -25
+    lens = np.asarray([5, 0, 37, 41], dtype=np.int32)
+    x = workloads.scores_cpu((4, 3, 40, 40), dtype, 1.0, seed=46)
+    y_st = oracle.softmax(workloads.to_storage(x), lens, 0.7, dtype)
+    dy = workloads.scores_cpu((4, 3, 40, 40), dtype, 1.0, seed=47)
+    ref = oracle.backward_f64(y_st, workloads.to_storage(dy), lens, 0.7, dtype)
+    y_t = workloads.from_storage(y_st, dtype)
+    dx = torch.as_tensor(ref).to(y_t.dtype)
+    check_rows_backward_against_oracle(y_t, dy, dx, lens, 0.7, dtype, u, tiny, rows_per_call=16)
+    bad = dx.clone()
+    bad[2, 1, 20, 3] += 0.05
+    with pytest.raises(AssertionError, match="beyond the bound"):
+        check_rows_backward_against_oracle(y_t, dy, bad, lens, 0.7, dtype, u, tiny,
+                                           rows_per_call=16)
+    bad = dx.clone()
+    bad[0, 2, 4, 5] = 1e-3
+    with pytest.raises(AssertionError, match="masked region"):
+        check_rows_backward_against_oracle(y_t, dy, bad, lens, 0.7, dtype, u, tiny,
+                                           rows_per_call=16)

@@ -17,8 +17,8 @@ import pytest
 
 import oracle
 import workloads
-from gtms_check import (bits, check_planes_backward_against_oracle, kept_mask, kept_row,
-                        path_ok, to_f64)
+from gtms_check import (bits, check_planes_backward_against_oracle,
+                        check_rows_backward_against_oracle, kept_mask, kept_row, path_ok, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -169,5 +169,26 @@ def test_backward_full_workload(name):
     worst = check_planes_backward_against_oracle(y, dy, dx, lens, w.scale, w.dtype, U[w.dtype],
                                                  TINY[w.dtype])
     print(f"{name}: every plane of the backward checked, worst error {worst:.3g}", flush=True)
+    del y, dy, dx
+    torch.cuda.empty_cache()
+
+
+def test_backward_full_long_rows():
+    """The 65536-wide-row workload (bf16 2 x 2 x 65536, the block path at eight vectors per
+    lane) at full size: y uniform in [0, 2/S), dy normal; every element against the oracle's
+    backward row entry point, in blocks of 512 rows."""
+    w = workloads.WORKLOADS["long_bf16_2x2x65536"]
+    lens = workloads.seq_lens(w)
+    print(f"backward full workload {w.name} lens={list(lens)}", flush=True)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4244)
+    y = torch.rand(w.shape, generator=gen, device="cuda",
+                   dtype=workloads.torch_dtype(w.dtype)).mul_(2.0 / w.S)
+    dy = workloads.scores_device(w.shape, w.dtype, 1.0, 4245)
+    dx = g.backward(y, dy, torch.as_tensor(lens).cuda(), w.scale)
+    torch.cuda.synchronize()
+    worst = check_rows_backward_against_oracle(y, dy, dx, lens, w.scale, w.dtype, U[w.dtype],
+                                               TINY[w.dtype])
+    print(f"{w.name}: every element of the backward checked, worst error {worst:.3g}", flush=True)
     del y, dy, dx
     torch.cuda.empty_cache()
