@@ -147,23 +147,34 @@ def check_planes_against_oracle(x_dev, y_dev, lens, scale: float, dtype: int,
 
 def check_planes_backward_against_oracle(y_dev, dy_dev, dx_dev, lens, scale: float, dtype: int,
                                          u: float, tiny: float, chunk_bytes: int = 4 << 30,
-                                         row_block: int = 1024) -> float:
+                                         row_block: int = 1024, plane_ref=None) -> float:
     """Every element of a backward result dx [B, M, S, S] on the device against the oracle's
     fp64 backward of the same y and dy: masked elements +0 bit for bit; kept elements finite
     and within u * |dx_ref| + 1e-5 * |scale| * y_c * max_k |dy_k| + tiny (max over the row's
     kept columns). Planes go to the host in chunks of at most chunk_bytes (three tensors),
     one oracle call per plane on host threads; a plane is compared in blocks of row_block rows.
-    Returns the max abs error on kept elements."""
+    Returns the max abs error on kept elements.
+
+    plane_ref(y_plane, dy_plane, p) -> (ref [S, S] fp64, keep [S, S] bool) gives the reference
+    and kept set of flat plane p from its raw inputs [1, 1, S, S]; by default the grouped tril
+    mask with the lengths `lens` (the mask variants pass their own)."""
     import oracle
 
     B, M, S, _ = dx_dev.shape
     es = esize(dtype)
     flat = [t.reshape(B * M, S, S) for t in (y_dev, dy_dev, dx_dev)]
-    keeps = {}
-    for b in range(B):
-        L = min(max(int(lens[b]), 0), S)
-        if L not in keeps:
-            keeps[L] = kept_mask(S, L)
+    if plane_ref is None:
+        keeps = {}
+        for b in range(B):
+            L = min(max(int(lens[b]), 0), S)
+            if L not in keeps:
+                keeps[L] = kept_mask(S, L)
+
+        def plane_ref(y_plane, dy_plane, p):
+            b = p // M
+            ref = oracle.backward_f64(y_plane, dy_plane, lens[b:b + 1], scale, dtype)[0, 0]
+            return ref, keeps[min(max(int(lens[b]), 0), S)]
+
     per_chunk = max(1, chunk_bytes // (3 * S * S * es))
     worst = 0.0
     with ThreadPoolExecutor(max_workers=host_threads()) as pool:
@@ -173,16 +184,14 @@ def check_planes_backward_against_oracle(y_dev, dy_dev, dx_dev, lens, scale: flo
 
             def one(i, ys=ys, gs=gs, ds=ds, p0=p0):
                 p = p0 + i
-                b = p // M
-                L = min(max(int(lens[b]), 0), S)
-                keep = keeps[L]
-                ref = oracle.backward_f64(ys[i:i + 1][None], gs[i:i + 1][None], lens[b:b + 1],
-                                          scale, dtype)[0, 0]
+                ref, keep = plane_ref(ys[i:i + 1][None], gs[i:i + 1][None], p)
                 assert not bits(ds[i])[~keep].any(), f"nonzero bits in masked region of plane {p}"
                 e = 0.0
-                for r0 in range(0, min(L, S), row_block):
-                    r1 = min(L, r0 + row_block)
+                for r0 in range(0, S, row_block):
+                    r1 = min(S, r0 + row_block)
                     k = keep[r0:r1]
+                    if not k.any():
+                        continue
                     got = to_f64(ds[i, r0:r1], dtype)
                     yv = to_f64(ys[i, r0:r1], dtype)
                     gv = np.where(k, np.abs(to_f64(gs[i, r0:r1], dtype)), 0.0)
@@ -192,7 +201,7 @@ def check_planes_backward_against_oracle(y_dev, dy_dev, dx_dev, lens, scale: flo
                     assert np.all(np.isfinite(got[k])), f"non-finite kept output in plane {p}"
                     bad = k & ~(err <= bound)
                     assert not bad.any(), \
-                        f"plane {p} (b={b}): {int(bad.sum())} kept elements beyond the bound"
+                        f"plane {p}: {int(bad.sum())} kept elements beyond the bound"
                     e = max(e, float(np.max(np.where(k, err, 0.0))))
                 return e
 

@@ -16,7 +16,8 @@ import pytest
 
 import oracle
 import workloads
-from gtms_check import TOL, bits, check_planes_against_oracle, kept_row, path_ok, to_f64
+from gtms_check import (TOL, bits, check_planes_against_oracle, check_planes_backward_against_oracle,
+                        kept_row, path_ok, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -375,3 +376,51 @@ def test_full_size_window_and_key_masks():
         return ref, np.broadcast_to(key[b, 0, 0].astype(bool), (S, S))
     worst = check_planes_against_oracle(x, y, None, w.scale, w.dtype, plane_ref=ref_key)
     print(f"key masks on {w.name}: every plane checked, worst error {worst:.3g}", flush=True)
+
+
+def test_full_size_window_and_key_mask_backwards():
+    """The backwards of the full-size variants, every element of every plane against the
+    oracle's variant backwards: a causal window of 512 columns on binary16 32 x 1 x 4096, and
+    per-sample key masks [B, 1, 1, S] on binary32 3 x 64 x 1000. y is drawn uniform in
+    [0, 2/S) (the backward is defined for any y), dy normal."""
+    w = workloads.WORKLOADS["scaled_f16_32x1x4096"]
+    lens = workloads.seq_lens(w)
+    S = w.S
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4301)
+    y = torch.rand(w.shape, generator=gen, device="cuda",
+                   dtype=workloads.torch_dtype(w.dtype)).mul_(2.0 / S)
+    dy = workloads.scores_device(w.shape, w.dtype, 1.0, 4302)
+    dx = g.backward_band(y, dy, torch.as_tensor(lens).cuda(), -511, 0, w.scale)
+    torch.cuda.synchronize()
+
+    def ref_band(y_plane, dy_plane, p):
+        b = p // w.M
+        ref = oracle.band_backward_f64(y_plane, dy_plane, lens[b:b + 1], -511, 0, w.scale,
+                                       w.dtype)[0, 0]
+        return ref, band_keep(S, lens[b], -511, 0)
+    worst = check_planes_backward_against_oracle(y, dy, dx, lens, w.scale, w.dtype, U[w.dtype],
+                                                 TINY[w.dtype], plane_ref=ref_band)
+    print(f"window tril(512) backward on {w.name}: every plane checked, worst error {worst:.3g}",
+          flush=True)
+    del y, dy, dx
+
+    w = workloads.WORKLOADS["readme_f32_3x64x1000"]
+    S = w.S
+    key = (np.arange(S)[None, :] < np.asarray([700, 1000, 10])[:, None]).astype(np.uint8)
+    key = key.reshape(w.B, 1, 1, S)
+    gen.manual_seed(4303)
+    y = torch.rand(w.shape, generator=gen, device="cuda").mul_(2.0 / S)
+    dy = workloads.scores_device(w.shape, w.dtype, 1.0, 4304)
+    dx = g.backward_masked(y, dy, torch.as_tensor(key).cuda(), None, w.scale)
+    torch.cuda.synchronize()
+
+    def ref_key(y_plane, dy_plane, p):
+        b = p // w.M
+        ref = oracle.masked_backward_f64(y_plane, dy_plane, key[b:b + 1], None, w.scale,
+                                         w.dtype)[0, 0]
+        return ref, np.broadcast_to(key[b, 0, 0].astype(bool), (S, S))
+    worst = check_planes_backward_against_oracle(y, dy, dx, None, w.scale, w.dtype, U[w.dtype],
+                                                 TINY[w.dtype], plane_ref=ref_key)
+    print(f"key mask backward on {w.name}: every plane checked, worst error {worst:.3g}",
+          flush=True)
