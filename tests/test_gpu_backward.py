@@ -97,11 +97,11 @@ def test_backward_widest_wave_rows(dtype):
     run_case((2, 1, 4000, 4000), dtype, [4000, 1401], 0.6, "wave", seed=400)
 
 
-def test_backward_block_rows_sampled():
+def test_backward_block_rows_every_element():
     """Rows that fill the block path's registers (binary16 40000 and bfloat16 65536 at eight
     16-byte vectors per lane, binary32 65536 forced to sixteen), y uniform in [0, 2/L) (rows
     that sum to about 1, like the forward's outputs the error bound is derived for), dy
-    normal; sampled rows against the oracle's row entry point."""
+    normal; every element against the oracle's backward row entry point, in blocks of rows."""
     for dtype, S, path in ((workloads.F16, 40000, "auto"), (workloads.BF16, 65536, "auto"),
                            (workloads.F32, 65536, "block")):
         L = S - 17
@@ -115,14 +115,10 @@ def test_backward_block_rows_sampled():
         sl = torch.as_tensor(np.asarray([L], dtype=np.int32)).cuda()
         dx = g.backward(y, dy, sl, 0.3, path=path)
         torch.cuda.synchronize()
-        rng = np.random.default_rng(S)
-        rs = sorted(set(int(r) for r in rng.choice(L, 12, replace=False)) |
-                    {0, L // 2, L - 1, L, S - 1})
-        y_st = workloads.to_storage(torch.stack([y[0, 0, r] for r in rs]).cpu())
-        g_st = workloads.to_storage(torch.stack([dy[0, 0, r] for r in rs]).cpu())
-        d_st = workloads.to_storage(torch.stack([dx[0, 0, r] for r in rs]).cpu())
-        ref = oracle.backward_rows_f64(y_st, g_st, rs, [L] * len(rs), 0.3, dtype)
-        check_rows(d_st, ref, y_st, g_st, [L] * len(rs), rs, 0.3, dtype)
+        worst = check_rows_backward_against_oracle(y, dy, dx, np.asarray([L], np.int32), 0.3,
+                                                   dtype, U[dtype], TINY[dtype])
+        print(f"S={S} {path}: every element of the backward checked, worst error {worst:.3g}",
+              flush=True)
         del y, dy, dx
         torch.cuda.empty_cache()
 
