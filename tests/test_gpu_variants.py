@@ -17,7 +17,8 @@ import pytest
 import oracle
 import workloads
 from gtms_check import (TOL, bits, check_planes_against_oracle, check_planes_backward_against_oracle,
-                        kept_row, path_ok, to_f64)
+                        check_rows_against_oracle, check_rows_backward_against_oracle, path_ok,
+                        to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -281,35 +282,24 @@ def test_variants_widest_wave_rows(dtype):
                keep_m, scale, dtype, "masked bwd wave")
 
 
-def test_variants_block_rows_sampled():
+def test_variants_block_rows_every_element():
     """Rows that fill the block path's registers (binary16 40000, bfloat16 65536: eight
     16-byte vectors per lane). A band [-S, 0] and a lower-triangular mask of ones, both
-    with the valid length, keep exactly the grouped tril set, so sampled rows compare with
-    the oracle's tril row entry points, forward and backward."""
+    with the valid length, keep exactly the grouped tril set, so every element compares with
+    the oracle's tril row entry points, forward and backward, in blocks of rows."""
     for dtype, S in ((workloads.F16, 40000), (workloads.BF16, 65536)):
         L = S - 17
+        lens = np.asarray([L], np.int32)
         print(f"variant block rows S={S} {DNAME[dtype]}", flush=True)
         sl = lens_dev([L])
         tril = torch.ones((S, S), dtype=torch.uint8, device="cuda").tril_()[None, None]
-        rng = np.random.default_rng(S)
-        rs = sorted(set(int(r) for r in rng.choice(L, 10, replace=False)) |
-                    {0, L // 2, L - 1, L, S - 1})
-
-        def rows_of(t):
-            return workloads.to_storage(torch.stack([t[0, 0, r] for r in rs]).cpu())
-
-        def check_fwd(out, xs, tag):
-            ref = oracle.softmax_rows_f64(xs, rs, [L] * len(rs), 0.5, dtype)
-            st = rows_of(out)
-            keep = np.stack([kept_row(S, L, r) for r in rs])
-            assert not bits(st)[~keep].any(), tag
-            err = np.abs(to_f64(st, dtype) - ref)[keep]
-            assert float(err.max()) <= TOL[dtype], (tag, float(err.max()))
-
         x = workloads.scores_device((1, 1, S, S), dtype, 1.0, S + 2)
-        xs = rows_of(x)
-        check_fwd(g.forward_band(x, sl, -S, 0, 0.5), xs, "band")
-        check_fwd(g.forward_masked(x, tril, sl, 0.5), xs, "masked")
+        for tag, out in (("band", g.forward_band(x, sl, -S, 0, 0.5)),
+                         ("masked", g.forward_masked(x, tril, sl, 0.5))):
+            torch.cuda.synchronize()
+            worst = check_rows_against_oracle(x, out, lens, 0.5, dtype)
+            print(f"S={S} {tag}: every element checked, worst error {worst:.3g}", flush=True)
+            del out
         del x
         torch.cuda.empty_cache()
         gen = torch.Generator(device="cuda")
@@ -318,27 +308,16 @@ def test_variants_block_rows_sampled():
         y = torch.rand((1, 1, S, S), generator=gen, device="cuda").mul_(2.0 / L).to(
             workloads.torch_dtype(dtype))
         dy = workloads.scores_device((1, 1, S, S), dtype, 1.0, S + 3)
-        ys, gs = rows_of(y), rows_of(dy)
-        ref = oracle.backward_rows_f64(ys, gs, rs, [L] * len(rs), 0.5, dtype)
-        keep = np.stack([kept_row(S, L, r) for r in rs])
         for tag, run in (("band bwd", lambda: g.backward_band(y, dy, sl, -S, 0, 0.5)),
                          ("masked bwd", lambda: g.backward_masked(y, dy, tril, sl, 0.5))):
             dx = run()
             torch.cuda.synchronize()
-            grad_check_rows(rows_of(dx), ref, ys, gs, keep, 0.5, dtype, tag)
+            worst = check_rows_backward_against_oracle(y, dy, dx, lens, 0.5, dtype, U[dtype],
+                                                       TINY[dtype])
+            print(f"S={S} {tag}: every element checked, worst error {worst:.3g}", flush=True)
             del dx
         del y, dy, tril
         torch.cuda.empty_cache()
-
-
-def grad_check_rows(st, ref, y_st, dy_st, keep, scale, dtype, tag):
-    """grad_check on sampled rows ([n, S] arrays)."""
-    assert not bits(st)[~keep].any(), f"{tag}: nonzero bits outside the kept set"
-    got, yv, gv = to_f64(st, dtype), to_f64(y_st, dtype), to_f64(dy_st, dtype)
-    gmax = np.max(np.where(keep, np.abs(gv), 0.0), axis=-1, keepdims=True)
-    bound = U[dtype] * np.abs(ref) + 1e-5 * abs(scale) * yv * gmax + TINY[dtype]
-    err = np.abs(got - ref)
-    assert np.all(err[keep] <= bound[keep]), f"{tag}: {float(np.max((err - bound)[keep]))}"
 
 
 def test_full_size_window_and_key_masks():
