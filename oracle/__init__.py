@@ -287,12 +287,18 @@ _default: Oracle | None = None
 
 
 def default() -> Oracle:
-    """The oracle built from ``gtms_oracle.c`` (rebuilt when the source is newer)."""
+    """The oracle built from ``gtms_oracle.c`` (rebuilt when the source is newer), or the
+    build named by the environment variable GTMS_ORACLE_LIB (the sanitizer test runs the pins
+    against an AddressSanitizer / UndefinedBehaviorSanitizer build that way)."""
     global _default
     if _default is None:
-        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
-            build()
-        _default = Oracle(LIB)
+        override = os.environ.get("GTMS_ORACLE_LIB")
+        if override:
+            _default = Oracle(override)
+        else:
+            if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+                build()
+            _default = Oracle(LIB)
     return _default
 
 

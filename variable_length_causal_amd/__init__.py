@@ -19,7 +19,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libgtms.so")
+# GTMS_LIBRARY names another build of the same library (the CPU sanitizer test loads one whose
+# host code is built with AddressSanitizer); by default the in-tree build
+LIB_PATH = os.environ.get("GTMS_LIBRARY") or os.path.join(HERE, "libgtms.so")
 
 # element-type, path and flag codes of include/gtms.h
 F32, F16, BF16 = 0, 1, 2
