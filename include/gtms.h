@@ -203,8 +203,14 @@ int gtms_backward_masked(const void* y, const void* dy, void* dx, const uint8_t*
  *               and the sums are fp32; the probabilities are rounded to `dtype` before the
  *               product with v (matrix-core operands); out is rounded to nearest-even.
  * D             64 or 128 (GTMS_ERR_PATH otherwise).
+ * scale         any finite value; 0 and -0 give the mean of v over the keys c <= r.
  * All pointers 16-byte aligned (GTMS_ERR_ALIGN). One head (S * D elements) must be below
  * 2^30 elements. The S x S scores are never written to memory.
+ * Values at positions >= L_b of q, k and v are never read into a result. Below L_b, v
+ * must be finite: the products of up to 127 later keys of the same 128-row query tile
+ * are formed with probability 0, so a NaN or infinity in v[c] can reach rows r < c of
+ * that tile (0 * inf is NaN). Non-finite q or k below L_b affect only the rows that
+ * attend to them.
  */
 int gtms_attention_forward(const void* q, const void* k, const void* v, void* out,
                            const int32_t* seq_lens, int64_t B, int64_t M, int64_t S, int64_t D,

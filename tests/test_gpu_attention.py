@@ -81,6 +81,19 @@ def test_attention_shapes(dtype, D):
         run_case(len(lens), 2, S, D, dtype, lens, 1.0 / np.sqrt(D), seed=10 * S + D)
 
 
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DNAME[d])
+@pytest.mark.parametrize("D", [64, 128])
+def test_attention_zero_and_negative_scales(dtype, D):
+    """Any finite scale is accepted (the ScaledMaskSoftmax article multiplies the scores by
+    it before the softmax): 0 and -0 give the running mean of v over the kept keys, and a
+    negative scale takes the softmax of the negated scores. Lengths cover several query
+    tiles, a partial tile, padded batches and a length past S."""
+    S = 300
+    lens = [S, 100, 0, S + 7]
+    for scale in (0.0, -0.0, -0.125):
+        run_case(len(lens), 2, S, D, dtype, lens, scale, seed=700 + D)
+
+
 def test_attention_scales_and_long_rows():
     run_case(2, 2, 1000, 64, workloads.BF16, [1000, 611], 0.3, seed=5)
     run_case(1, 1, 700, 128, workloads.F16, [700], 0.05, seed=6)

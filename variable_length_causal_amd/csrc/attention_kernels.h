@@ -141,14 +141,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3
     // Q^T as the B operand: lane l holds Q[row][16*kk + 8*g + j]
     const rsrc_t qin = make_rsrc((const char*)a.q + head * 2, head_bytes);
     // A negative scale is applied as |scale| to -Q (a sign-bit flip, exact), so that the
-    // row max is always the max of the raw scores.
+    // row max is always the max of the raw scores. A scale of +-0 (or one whose k2 is below
+    // the smallest normal float) makes every kept score 0, so that softmax is uniform over
+    // the kept keys: Q is zeroed and k2 set to 1. Masked keys (score -inf) then still meet
+    // a positive factor, where -inf * 0 would give NaN.
+    const bool zero_scale = fabsf(a.k2) < __FLT_MIN__;
     const uint32_t qsign = a.k2 < 0.0f ? 0x80008000u : 0u;
-    const float k2 = fabsf(a.k2);
+    const uint32_t qkeep = zero_scale ? 0u : 0xffffffffu;
+    const float k2 = zero_scale ? 1.0f : fabsf(a.k2);
     vec8 qf[D / 16];
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
-        qf[kk] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(
-                                              qin, (row * D + 16 * kk + 8 * g) * 2, 0, 0) ^ qsign);
+        qf[kk] = __builtin_bit_cast(
+            vec8, (__builtin_amdgcn_raw_buffer_load_b128(qin, (row * D + 16 * kk + 8 * g) * 2, 0, 0) ^
+                   qsign) & qkeep);
     // K and V of this head, keys < L only (the range check zero-fills keys past L, so the
     // masked probabilities meet finite values)
     const uint32_t kv_bytes = (uint32_t)((uint64_t)L * D * 2);
