@@ -3,9 +3,9 @@
 
 One step is one call of the whole operation (gtms_forward: decomposition, padded rows,
 prefix loads, max, exp/sum, normalise, zero tails) over one batch of synthetic scores that
-are already resident in HBM. The default workload is the README's timed shape
-X[3, 64, 1000, 1000] in binary32 with seeded lengths; the other workloads are parity-test
-shapes and can be measured with --workload.
+are already resident in HBM. The default workload is the larger of the README's two timed
+binary32 shapes, X[12, 64, 1000, 1000] (its A10 timing at B = 12), with seeded lengths; the
+other workloads are parity-test shapes and can be measured with --workload.
 
 Prints ONE JSON line. value = effective HBM throughput over the algorithmic bytes of a
 step: the kept lower-triangle reads plus the full S*S writes,
@@ -394,7 +394,7 @@ def main():
         if args.workload not in workloads.ATTN_WORKLOADS:
             ap.error("--op attention takes an attention workload")
         return bench_attention(args)
-    args.workload = args.workload or "readme_f32_3x64x1000"
+    args.workload = args.workload or "readme_f32_12x64x1000"
     if args.workload not in workloads.WORKLOADS:
         ap.error(f"--op {args.op} takes a softmax workload")
     dev = torch.device("cuda:0")
