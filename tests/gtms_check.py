@@ -145,6 +145,36 @@ def check_planes_against_oracle(x_dev, y_dev, lens, scale: float, dtype: int,
     return worst
 
 
+def oracle_forward_to_device(x_dev, lens, scale: float, dtype: int,
+                             chunk_bytes: int = 4 << 30):
+    """The oracle's forward of a [B, M, S, S] device tensor, rounded into the element type and
+    returned as a new device tensor: planes go to the host in chunks of at most chunk_bytes,
+    one oracle call per plane on host threads, and the rounded planes are copied back. Lets a
+    full-size backward run on real softmax rows that do not come from the GPU path."""
+    import oracle
+    import torch
+
+    B, M, S, _ = x_dev.shape
+    xf = x_dev.reshape(B * M, S, S)
+    y_dev = torch.empty_like(x_dev)
+    yf = y_dev.reshape(B * M, S, S)
+    per_chunk = max(1, chunk_bytes // (2 * S * S * esize(dtype)))
+    with ThreadPoolExecutor(max_workers=host_threads()) as pool:
+        for p0 in range(0, B * M, per_chunk):
+            p1 = min(B * M, p0 + per_chunk)
+            xs = workloads.to_storage(xf[p0:p1].cpu())
+            ys = np.empty_like(xs)
+
+            def one(i, xs=xs, ys=ys, p0=p0):
+                b = (p0 + i) // M
+                ys[i] = oracle.softmax(xs[i:i + 1][None], lens[b:b + 1], scale, dtype)[0, 0]
+
+            list(pool.map(one, range(p1 - p0)))
+            yf[p0:p1].copy_(workloads.from_storage(ys, dtype))
+            del xs, ys
+    return y_dev
+
+
 def check_planes_backward_against_oracle(y_dev, dy_dev, dx_dev, lens, scale: float, dtype: int,
                                          u: float, tiny: float, chunk_bytes: int = 4 << 30,
                                          row_block: int = 1024, plane_ref=None) -> float:

@@ -9,7 +9,8 @@ import pytest
 import oracle
 import workloads
 from gtms_check import (TOL, check_planes_against_oracle, check_planes_backward_against_oracle,
-                        check_rows_against_oracle, check_rows_backward_against_oracle)
+                        check_rows_against_oracle, check_rows_backward_against_oracle,
+                        oracle_forward_to_device)
 
 torch = pytest.importorskip("torch")
 
@@ -112,3 +113,17 @@ def test_row_block_backward_checker():
     with pytest.raises(AssertionError, match="masked region"):
         check_rows_backward_against_oracle(y_t, dy, bad, lens, 0.7, dtype, u, tiny,
                                            rows_per_call=16)
+
+
+@pytest.mark.parametrize("dtype", [workloads.F32, workloads.F16, workloads.BF16])
+def test_oracle_forward_to_device(dtype):
+    """The chunked, per-plane, threaded forward that builds the full-size backward's y gives
+    the bits of one oracle call over the whole tensor."""
+    lens = np.asarray([5, 0, 37, 41], dtype=np.int32)
+    x = workloads.scores_cpu((4, 3, 40, 40), dtype, 1.0, seed=48)
+    whole = oracle.softmax(workloads.to_storage(x), lens, 0.7, dtype)
+    chunk = 5 * 2 * 40 * 40 * (4 if dtype == workloads.F32 else 2)
+    y = oracle_forward_to_device(x, lens, 0.7, dtype, chunk_bytes=chunk)
+    assert y.dtype == x.dtype and tuple(y.shape) == tuple(x.shape)
+    got = workloads.to_storage(y)
+    assert np.array_equal(got.view(np.uint8), whole.view(np.uint8))

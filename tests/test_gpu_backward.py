@@ -1,8 +1,9 @@
 """GPU parity of the backward kernels against the oracle's backward.
 
 The forward output y and the upstream gradient dy are inputs of both sides: y comes from the
-oracle's rounded forward (small shapes) or a seeded uniform draw (full shapes), never from
-the GPU path. Masked elements of dx must be +0 bit for bit. Kept elements must satisfy, per
+oracle's rounded forward (small shapes and the four benchmark workloads at full size) or,
+for rows of 40000 elements and more, a seeded uniform draw whose rows sum to about 1; never
+from the GPU path. Masked elements of dx must be +0 bit for bit. Kept elements must satisfy, per
 element, the bound derived from the fp32 arithmetic:
     |dx_gpu - dx_ref| <= u * |dx_ref| + 1e-5 * scale * y_c * max_k |dy_k|
 with u = 2^-21 (binary32), 2^-10 (binary16), 2^-7 (bfloat16): the output rounding plus a
@@ -18,7 +19,8 @@ import pytest
 import oracle
 import workloads
 from gtms_check import (bits, check_planes_backward_against_oracle,
-                        check_rows_backward_against_oracle, kept_mask, kept_row, path_ok, to_f64)
+                        check_rows_backward_against_oracle, kept_mask, kept_row,
+                        oracle_forward_to_device, path_ok, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -84,6 +86,61 @@ def test_backward_shape_sweep(dtype):
                 run_case((4, 2, S, S), dtype, lens, 0.7, path, seed=100 + S)
 
 
+# Row lengths where the automatic choice changes kernel (see test_gpu_parity.SWITCH_CASES):
+# the backward takes the same choice, by the same rule over its row slots.
+SWITCH_CASES = [
+    (workloads.F32, 1000, 0, "wave"), (workloads.F32, 1004, 0, "block"),
+    (workloads.F32, 1008, 0, "wave"), (workloads.F32, 1012, 0, "block"),
+    (workloads.F32, 1020, 0, "block"), (workloads.F32, 1024, 0, "wave"),
+    (workloads.F32, 1028, 0, "block"), (workloads.F32, 1032, 0, "block"),
+    (workloads.F32, 1024, 16, "block"),
+] + [(dt, S, off, path) for dt in (workloads.F16, workloads.BF16) for S, off, path in (
+    (2040, 0, "block"), (2047, 0, "block"), (2048, 0, "wave"), (2049, 0, "block"),
+    (2056, 0, "block"), (2048, 16, "block"))]
+
+
+def offset_copy(host, dtype, offset_bytes):
+    """A device copy of a CPU tensor whose data starts offset_bytes past a 256-byte boundary."""
+    es = 4 if dtype == workloads.F32 else 2
+    n = host.numel()
+    buf = torch.zeros(n + 256 // es, dtype=host.dtype, device="cuda")
+    t = buf[offset_bytes // es:offset_bytes // es + n].view(host.shape)
+    assert t.data_ptr() % 256 == offset_bytes
+    t.copy_(host.cuda())
+    return t
+
+
+@pytest.mark.parametrize("case", SWITCH_CASES,
+                         ids=lambda c: f"{DNAME[c[0]]}-{c[1]}-off{c[2]}-{c[3]}")
+def test_backward_auto_path_switch_sizes(case):
+    """The backward through the automatic choice at the row lengths where it changes kernel,
+    lengths S, S - 1, S / 2 and 0, y from the oracle's forward: every element within the
+    bound, and the same bits as the path the choice rule names."""
+    dtype, S, off, expect = case
+    lens = [S, S - 1, S // 2, 0]
+    shape = (len(lens), 2, S, S)
+    x = workloads.scores_cpu(shape, dtype, 1.0, 3600 + S + off)
+    y_st = oracle.softmax(workloads.to_storage(x), lens, 0.8, dtype)
+    dy = workloads.scores_cpu(shape, dtype, 1.0, 3601 + S + off)
+    dy_st = workloads.to_storage(dy)
+    ref = oracle.backward_f64(y_st, dy_st, lens, 0.8, dtype)
+    sl = torch.as_tensor(np.asarray(lens, dtype=np.int32)).cuda()
+    y_dev = offset_copy(workloads.from_storage(y_st, dtype), dtype, off)
+    dy_dev = offset_copy(dy, dtype, off)
+    got = {}
+    for path in ("auto", expect):
+        dx = offset_copy(torch.zeros_like(dy), dtype, off)
+        print(f"backward switch S={S} dtype={DNAME[dtype]} offset={off} path={path}", flush=True)
+        g.backward(y_dev, dy_dev, sl, 0.8, out=dx, path=path)
+        torch.cuda.synchronize()
+        got[path] = workloads.to_storage(dx.cpu())
+    n = len(lens) * 2 * S
+    check_rows(got["auto"].reshape(n, S), ref.reshape(n, S), y_st.reshape(n, S),
+               dy_st.reshape(n, S), np.repeat(np.asarray(lens), 2 * S),
+               np.tile(np.arange(S), len(lens) * 2), 0.8, dtype)
+    assert np.array_equal(bits(got["auto"]), bits(got[expect]))
+
+
 def test_backward_long_rows():
     for dtype, S, lens in ((workloads.F16, 4096, [4096, 1500]), (workloads.BF16, 8192, [8000])):
         for path in ("auto", "block", "stream"):
@@ -147,17 +204,17 @@ def test_backward_in_place_and_poison():
 @pytest.mark.parametrize("name", ["readme_f32_3x64x1000", "readme_f32_12x64x1000",
                                   "scaled_f16_32x1x4096", "skewed_bf16_8x32x8192"])
 def test_backward_full_workload(name):
-    """A benchmark workload at full size through the default entry point: y drawn uniform in
-    [0, 2/S) (the backward is defined for any y; rows summing to about 1, like the forward's
-    outputs the error bound is derived for), dy normal; every element of every plane against
-    the oracle's backward."""
+    """A benchmark workload at full size through the default entry point, on real softmax
+    rows: y is the oracle's rounded forward of the workload's own seeded scores (one-hot row
+    0, peaked short rows, rows of every length up to S), dy normal; every element of every
+    plane against the oracle's backward."""
     w = workloads.WORKLOADS[name]
     lens = workloads.seq_lens(w)
     print(f"backward full workload {name} lens={list(lens)}", flush=True)
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(4242)
-    y = torch.rand(w.shape, generator=gen, device="cuda",
-                   dtype=workloads.torch_dtype(w.dtype)).mul_(2.0 / w.S)
+    x = workloads.scores_device(w.shape, w.dtype, w.sigma, w.x_seed)
+    y = oracle_forward_to_device(x, lens, w.scale, w.dtype)
+    del x
+    torch.cuda.empty_cache()
     dy = workloads.scores_device(w.shape, w.dtype, 1.0, 4243)
     sl = torch.as_tensor(lens).cuda()
     dx = g.backward(y, dy, sl, w.scale)

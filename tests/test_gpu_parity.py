@@ -77,6 +77,59 @@ def test_shape_sweep(dtype):
             check_against_oracle(workloads.to_storage(y.cpu()), ref, lens, dtype)
 
 
+# Row lengths at which the automatic choice moves between the one-wavefront path and the
+# block path. A wavefront holds 256 slots of 16 bytes; a row needs ceil(S / VEC) of them
+# plus the slots it may write of its predecessor's last 128-byte line, (128 - gcd(row
+# bytes, 128)) / 16 on a 128-byte aligned tensor and 7 on one that is not. Rows whose byte
+# length is not a multiple of 16 take element accesses (one slot per element). Each case
+# names the path the rule gives; the automatic call must match that forced path bit for bit.
+SWITCH_CASES = [
+    (workloads.F32, 1000, 0, "wave"), (workloads.F32, 1004, 0, "block"),
+    (workloads.F32, 1008, 0, "wave"), (workloads.F32, 1012, 0, "block"),
+    (workloads.F32, 1016, 0, "block"), (workloads.F32, 1020, 0, "block"),
+    (workloads.F32, 1024, 0, "wave"), (workloads.F32, 1028, 0, "block"),
+    (workloads.F32, 1032, 0, "block"), (workloads.F32, 1000, 16, "block"),
+    (workloads.F32, 1024, 16, "block"),
+] + [(dt, S, off, path) for dt in (workloads.F16, workloads.BF16) for S, off, path in (
+    (2032, 0, "block"), (2040, 0, "block"), (2047, 0, "block"), (2048, 0, "wave"),
+    (2049, 0, "block"), (2056, 0, "block"), (2048, 16, "block"))]
+
+
+def offset_tensor(shape, dtype, offset_bytes):
+    """A zeroed device tensor whose data starts offset_bytes past a 256-byte boundary."""
+    tdt = workloads.torch_dtype(dtype)
+    es = 4 if dtype == workloads.F32 else 2
+    n = int(np.prod(shape))
+    buf = torch.zeros(n + 256 // es, dtype=tdt, device="cuda")
+    t = buf[offset_bytes // es:offset_bytes // es + n].view(shape)
+    assert t.data_ptr() % 256 == offset_bytes
+    return t
+
+
+@pytest.mark.parametrize("case", SWITCH_CASES,
+                         ids=lambda c: f"{DNAME[c[0]]}-{c[1]}-off{c[2]}-{c[3]}")
+def test_auto_path_switch_sizes(case):
+    """Forward through the automatic choice at the row lengths where it changes kernel,
+    lengths S, S - 1, S / 2 and 0: every element against the oracle, and the same bits as
+    the path the choice rule names."""
+    dtype, S, off, expect = case
+    lens = [S, S - 1, S // 2, 0]
+    x_cpu = workloads.scores_cpu((len(lens), 2, S, S), dtype, 1.0, seed=3500 + S + off)
+    ref = oracle.softmax_f64(workloads.to_storage(x_cpu), lens, 0.8, dtype)
+    sl = torch.as_tensor(np.asarray(lens, dtype=np.int32)).cuda()
+    got = {}
+    for path in ("auto", expect):
+        x = offset_tensor(x_cpu.shape, dtype, off)
+        x.copy_(x_cpu.cuda())
+        out = offset_tensor(x_cpu.shape, dtype, off)
+        print(f"switch S={S} dtype={DNAME[dtype]} offset={off} path={path}", flush=True)
+        g.forward(x, sl, 0.8, out=out, path=path)
+        torch.cuda.synchronize()
+        got[path] = workloads.to_storage(out.cpu())
+    check_against_oracle(got["auto"], ref, lens, dtype)
+    assert np.array_equal(bits(got["auto"]), bits(got[expect]))
+
+
 @pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DNAME[d])
 def test_unaligned_rows_take_the_scalar_path(dtype):
     """A tensor that starts off a 16-byte boundary, and rows whose byte length is not a
