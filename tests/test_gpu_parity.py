@@ -54,7 +54,8 @@ def test_worked_example_shape():
     x = workloads.scores_cpu(w.shape, w.dtype, w.sigma, w.x_seed)
     lens = workloads.seq_lens(w)
     for path in ("auto", "wave", "block", "stream"):
-        check_small(x, lens, w.scale, w.dtype, path)
+        if path_ok(path, w.S, w.dtype):
+            check_small(x, lens, w.scale, w.dtype, path)
 
 
 S_SWEEP = [1, 2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 31, 33, 63, 64, 65, 127, 128, 129, 255, 256,
@@ -179,10 +180,11 @@ def test_long_rows_every_path():
 
 
 def test_very_long_rows_every_element():
-    """Rows beyond the block path's registers (binary32 70000 and bfloat16 100000, the stream
-    path) and at or near its limit (binary32 65536 forced to sixteen vectors per lane,
-    binary16 40000 through the automatic choice): every element against the oracle, in blocks
-    of 1024 rows through its row entry point."""
+    """Rows at the block path's widest layout, where each lane keeps sixteen raw 16-byte
+    vectors (bfloat16 100000 through the automatic choice, 12.2 vectors per lane with the
+    last one partly used; binary32 65536 forced, exactly sixteen), beyond it (binary32 70000,
+    the stream path) and at the automatic eight vectors per lane (binary16 40000): every
+    element against the oracle, in blocks of 1024 rows through its row entry point."""
     for dtype, S, path in ((workloads.F32, 70000, "stream"), (workloads.F32, 65536, "block"),
                            (workloads.BF16, 100000, "auto"), (workloads.F16, 40000, "auto")):
         lens = [S - 17]
@@ -364,6 +366,23 @@ def test_side_stream_and_graph_replay():
         assert torch.equal(dx.view(torch.int32), ref_dx.view(torch.int32)), f"replay {i}"
         g.forward(x, sl, 0.25)   # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_full_long_bf16_2x1x100000():
+    """Rows of 100000 bfloat16 elements (the block path at sixteen raw vectors per lane) at the
+    benchmark's size, lengths 100000 and 70000: every element against the oracle, in blocks of
+    1024 rows through the oracle's row entry point."""
+    name = "long_bf16_2x1x100000"
+    w = workloads.WORKLOADS[name]
+    lens = workloads.seq_lens(w)
+    print(f"full workload {name} lens={list(lens)}", flush=True)
+    x = workloads.scores_device(w.shape, w.dtype, w.sigma, w.x_seed)
+    y = g.forward(x, torch.as_tensor(lens).cuda(), w.scale)
+    torch.cuda.synchronize()
+    worst = check_rows_against_oracle(x, y, lens, w.scale, w.dtype)
+    print(f"{name}: every element checked, worst error {worst:.3g}", flush=True)
+    del x, y
+    torch.cuda.empty_cache()
 
 
 def test_full_long_bf16_2x2x65536():

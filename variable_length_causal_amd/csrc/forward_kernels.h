@@ -24,7 +24,9 @@
 //   fwd_wave   one wavefront per row, kept prefix held in registers (NV vectors per lane);
 //   fwd_block  one workgroup of W wavefronts per row, per-wave (max, sum) partials merged
 //              through LDS with the log-sum-exp rule of the split-KV reduction in
-//              ColossalAI's flash_decoding.py (_flash_decoding_fwd_reduce_kernel);
+//              ColossalAI's flash_decoding.py (_flash_decoding_fwd_reduce_kernel); at 16
+//              vectors per lane a lane keeps raw vectors only (RowPart's RAW mode), so that
+//              a workgroup of 16 wavefronts holds 256 KB of a row;
 //   fwd_stream one workgroup per row, two passes (online max/sum, then normalise) for rows
 //              too long for registers.
 // A work unit is one row, or optionally the pair (r, S-1-r), whose kept prefixes add up to
@@ -210,14 +212,21 @@ constexpr int kOutOfRange = (int)0x80000000u;  // an offset every buffer range c
 
 // Lanes holding this many elements or more run the LEAN variants of the row parts.
 constexpr int kLeanElems = 64;
+// Rows that need this many vectors per lane run the RAW variants: a lane keeps only its raw
+// 16-byte vectors (64 registers at 16 vectors), and the max, sum and write passes each unpack
+// them again; the write pass recomputes 2^(z - m) instead of keeping it. The fp32 values of 16
+// vectors (128 registers for 16-bit types) would not fit beside them: with RAW a workgroup of
+// 16 wavefronts holds 256 KB of a row (16-bit rows of 131072 elements, binary32 of 65536).
+constexpr int kRawNV = 16;
 
-template <class IO, int NA, int STRIDE, int MK, bool LEAN>
+template <class IO, int NA, int STRIDE, int MK, bool LEAN, bool RAW = false>
 struct RowPart {
     using MIO = MaskIo<IO::VEC>;
     typename IO::raw_t raw[NA];
     typename MIO::raw_t mk[MK == MK_MASK ? NA : 1];
-    float e[NA][IO::VEC];
+    float e[RAW ? 1 : NA][IO::VEC];
     float m, s;
+    float kk;  // RAW: the scale, kept for the write pass
 
     // Element q of the vector in slot j is kept when its column c = v*VEC + q lies in
     // [c0, c1] (and, for an explicit mask, its mask byte is non-zero): q >= ka and q < kc.
@@ -253,8 +262,110 @@ struct RowPart {
         }
     }
 
+    // RAW: every pass starts from opaque copies of the thread's position and the interval
+    // (fresh_pass), and each slot's raw vector (and mask bytes) passes through an opaque copy
+    // (raw_slot), so that no pass reuses another pass's unpacked values or keep bounds.
+    struct Fresh {
+        int t, hv;
+        Cols k;
+    };
+    __device__ __forceinline__ static Fresh fresh_pass(int t, int hv, const Cols& k) {
+        Fresh f{t, hv, k};
+        opaque(f.t);
+        opaque(f.hv);
+        opaque(f.k.c0);
+        opaque(f.k.c1);
+        return f;
+    }
+    // `after`: the previous slot's result; the copy takes it as an input, so that the slots
+    // are worked through one after another (otherwise every slot's values are computed
+    // first, and all of them are live at once).
+    __device__ __forceinline__ void raw_slot(const Fresh& fr, int j, float after, float (&f)[IO::VEC],
+                                             typename MIO::raw_t& mb, int& kc, int& ka) const {
+        typename IO::raw_t r = raw[j];
+        asm volatile("" : "+v"(r) : "v"(after));
+        IO::unpack(r, f);
+        mb = mask_of(j);
+        if constexpr (MK == MK_MASK) opaque(mb);
+        kc = kept_count(fr.t, j, fr.hv, fr.k);
+        ka = kept_from(fr.t, j, fr.hv, fr.k);
+    }
+    // RAW: what slot j holds for the whole wavefront (uniform): no kept element, only kept
+    // elements (never for an explicit mask, whose bytes decide), or a mix. Slots of a long
+    // row's thread often lie wholly before or past its interval, or wholly inside it.
+    enum : int { kSlotEmpty = 0, kSlotFull = 1, kSlotMixed = 2 };
+    __device__ __forceinline__ static int slot_class(int t, int j, int hv, const Cols& k) {
+        constexpr int VEC = IO::VEC;
+        const int lo = uniform(t & ~(kWave - 1)) + j * STRIDE - hv;  // the wave's first vector
+        const int hi = lo + kWave - 1;
+        if (hi < 0 || lo * VEC > k.c1 || hi * VEC + VEC - 1 < k.c0) return kSlotEmpty;
+        if (MK != MK_MASK && lo >= 0 && lo * VEC >= k.c0 && hi * VEC + VEC - 1 <= k.c1)
+            return kSlotFull;
+        return kSlotMixed;
+    }
+    __device__ __forceinline__ static float tree_sum(const float (&x)[IO::VEC]) {
+        if constexpr (IO::VEC == 1) {
+            return x[0];
+        } else {
+            float y[IO::VEC / 2];
+#pragma unroll
+            for (int i = 0; i < IO::VEC / 2; ++i) y[i] = x[2 * i] + x[2 * i + 1];
+#pragma unroll
+            for (int w = IO::VEC / 4; w >= 1; w /= 2)
+#pragma unroll
+                for (int i = 0; i < w; ++i) y[i] = y[2 * i] + y[2 * i + 1];
+            return y[0];
+        }
+    }
+
     __device__ __forceinline__ void compute(int t, int hv, const Cols& k, float kscale) {
         constexpr int VEC = IO::VEC;
+        if constexpr (RAW) {
+            kk = kscale;
+            m = -INFINITY;
+            const Fresh f1 = fresh_pass(t, hv, k);
+#pragma unroll
+            for (int j = 0; j < NA; ++j) {
+                const int sc = slot_class(t, j, hv, k);
+                if (sc == kSlotEmpty) continue;
+                float f[VEC];
+                typename MIO::raw_t mb;
+                int kc, ka;
+                raw_slot(f1, j, m, f, mb, kc, ka);
+                float lm = -INFINITY;
+                if (sc == kSlotFull) {
+#pragma unroll
+                    for (int q = 0; q < VEC; ++q) lm = fmaxf(lm, f[q] * kscale);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < VEC; ++q)
+                        lm = fmaxf(lm, kept(mb, q, ka, kc) ? f[q] * kscale : -INFINITY);
+                }
+                m = fmaxf(m, lm);
+            }
+            const float mm = m == -INFINITY ? 0.0f : m;
+            s = 0.0f;
+            const Fresh f2 = fresh_pass(t, hv, k);
+#pragma unroll
+            for (int j = 0; j < NA; ++j) {
+                const int sc = slot_class(t, j, hv, k);
+                if (sc == kSlotEmpty) continue;
+                float f[VEC];
+                typename MIO::raw_t mb;
+                int kc, ka;
+                raw_slot(f2, j, s, f, mb, kc, ka);
+                if (sc == kSlotFull) {
+#pragma unroll
+                    for (int q = 0; q < VEC; ++q) f[q] = __builtin_amdgcn_exp2f(f[q] * kscale - mm);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < VEC; ++q)
+                        f[q] = kept(mb, q, ka, kc) ? __builtin_amdgcn_exp2f(f[q] * kscale - mm) : 0.0f;
+                }
+                s += tree_sum(f);
+            }
+            return;
+        }
         m = -INFINITY;
 #pragma unroll
         for (int j = 0; j < NA; ++j) {
@@ -304,6 +415,33 @@ struct RowPart {
     __device__ __forceinline__ void write(rsrc_t out, int t, int hv, const Cols& k,
                                           float g) const {
         constexpr int VEC = IO::VEC;
+        if constexpr (RAW) {  // y = 2^(z - m) * g: the element's exponential again
+            const Fresh f3 = fresh_pass(t, hv, k);
+            float last = g;
+#pragma unroll
+            for (int j = 0; j < NA; ++j) {
+                const int sc = slot_class(t, j, hv, k);
+                if (sc == kSlotEmpty) {
+                    IO::template store<SP>(out, (t + j * STRIDE) * IO::BYTES, IO::zero());
+                    continue;
+                }
+                float f[VEC];
+                typename MIO::raw_t mb;
+                int kc, ka;
+                raw_slot(f3, j, last, f, mb, kc, ka);
+                if (sc == kSlotFull) {
+#pragma unroll
+                    for (int q = 0; q < VEC; ++q) f[q] = __builtin_amdgcn_exp2f(f[q] * kk - m) * g;
+                } else {
+#pragma unroll
+                    for (int q = 0; q < VEC; ++q)
+                        f[q] = kept(mb, q, ka, kc) ? __builtin_amdgcn_exp2f(f[q] * kk - m) * g : 0.0f;
+                }
+                last = f[VEC - 1];
+                IO::template store<SP>(out, (t + j * STRIDE) * IO::BYTES, IO::pack(f));
+            }
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < NA; ++j) {
             const int kc = fresh_if<LEAN>(kept_count(t, j, hv, k)),
@@ -349,7 +487,7 @@ __device__ __forceinline__ void wave_row(const FwdArgs& a, uint32_t plane, int r
                                      : in;
     const int hv = sp.hv;
     with_live_slots<NV>((nin + hv + kWave - 1) / kWave, [&]<int NA>() {
-        RowPart<IO, NA, kWave, MK, NV * IO::VEC >= kLeanElems> p;
+        RowPart<IO, NA, kWave, MK, NV * IO::VEC >= kLeanElems, NA >= kRawNV> p;
         p.load(in, min, lane, hv, k);
         write_zero_slots<IO, NA, NV, kWave, SP>(out, lane);
         p.compute(lane, hv, k, a.k);
@@ -382,6 +520,16 @@ __global__ __launch_bounds__(WPB * kWave) void fwd_wave(FwdArgs a) {
 template <int W>
 __device__ __forceinline__ void merge_partials(const float* pm, const float* ps, float& m,
                                                float& s) {
+    if constexpr (W >= 8) {
+        // lane w takes wave w's partial, and the merge is two wave reductions: two registers
+        // instead of 2 * W (a lane of a 16-wavefront workgroup has 128 in all)
+        const int lane = threadIdx.x & (kWave - 1);
+        const float pw = lane < W ? pm[lane] : -INFINITY;
+        const float sw = lane < W ? ps[lane] : 0.0f;
+        m = wave_reduce<OpMax>(pw);
+        s = wave_reduce<OpSum>(pw == -INFINITY ? 0.0f : sw * __builtin_amdgcn_exp2f(pw - m));
+        return;
+    }
     m = -INFINITY;
 #pragma unroll
     for (int w = 0; w < W; ++w) m = fmaxf(m, pm[w]);
@@ -411,7 +559,7 @@ __device__ __forceinline__ void block_row(const FwdArgs& a, uint32_t plane, int 
                                      : in;
     const int hv = sp.hv;
     with_live_slots<NV>((nin + hv + T - 1) / T, [&]<int NA>() {
-        RowPart<IO, NA, T, MK, NV * IO::VEC >= kLeanElems> p;
+        RowPart<IO, NA, T, MK, NV * IO::VEC >= kLeanElems, NA >= kRawNV> p;
         p.load(in, min, t, hv, k);
         write_zero_slots<IO, NA, NV, T, SP>(out, t);
         p.compute(t, hv, k, a.k);

@@ -70,16 +70,17 @@ int64_t line_slack(bool lines, int64_t row_bytes, const void* out) {
 // may write for its predecessor (line_slack).
 //   auto:   rows up to 256 slots -> one wavefront per row (NV <= 4); longer rows -> W
 //           wavefronts per row with NV = 4 (the stores of each instruction then cover
-//           W KB of the row); W = 16 and NV up to kAutoMaxNV beyond that; the stream path
+//           W KB of the row); W = 16 and NV up to auto_max_nv beyond that; the stream path
 //           last.
 //   forced: the named path if it can hold the row.
-int make_plan(int64_t S, int dtype, bool wide, int64_t slack, int path, Plan* p) {
+int make_plan(int64_t S, int dtype, bool wide, int64_t slack, int path, int64_t auto_max_nv,
+              Plan* p) {
     const int64_t vec = wide ? 16 / esize_of(dtype) : 1;
     const int64_t slots = cdiv(S, vec) + slack;  // vectors a row may span
     p->wide = wide;
     if (path == GTMS_PATH_AUTO) {
         if (slots <= kWave * kAutoNV) path = GTMS_PATH_WAVE;
-        else if (slots <= int64_t(kWave) * kMaxW * kAutoMaxNV) path = GTMS_PATH_BLOCK;
+        else if (slots <= int64_t(kWave) * kMaxW * auto_max_nv) path = GTMS_PATH_BLOCK;
         else path = GTMS_PATH_STREAM;
     }
     p->path = path;
@@ -152,7 +153,11 @@ int run_impl(const void* x, const void* g, void* out, const int32_t* seq_lens, i
     const int64_t row_bytes = S * esize_of(dtype);
     const bool lines = wide && row_bytes >= 128 && path != GTMS_PATH_STREAM;
     Plan plan;
-    st = make_plan(S, dtype, wide, line_slack(lines, row_bytes, out), path, &plan);
+    // the block path's widest automatic layout: 16 vectors per lane for the forward of the
+    // computed masks (their row parts keep raw vectors only, see RowPart), 8 otherwise
+    const int64_t auto_max_nv =
+        OP == OP_FWD && mk.kind != MK_MASK && wide ? kAutoMaxNVRaw : kAutoMaxNV;
+    st = make_plan(S, dtype, wide, line_slack(lines, row_bytes, out), path, auto_max_nv, &plan);
     if (st != GTMS_OK) return st;
 
     FwdArgs a;

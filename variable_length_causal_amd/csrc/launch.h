@@ -16,10 +16,16 @@ constexpr int kAutoNV = 4;      // vectors per lane the automatic choice aims fo
 // Vectors per lane the automatic choice takes at most on the block path; longer rows go to
 // the stream path. Measured on MI355X against forced paths: at NV = 8 the block kernels beat
 // the stream kernels (bfloat16 rows of 65536: forward 5930 vs 4979 GB/s, backward 6169 vs
-// 4953, explicit-mask backward 5332 vs 4044); at NV = 16 the row no longer fits in the 128
-// registers a lane of a 16-wavefront workgroup has, and the spilling kernels run 1.0-3.8x
-// slower than the stream kernels (bfloat16 rows of 98304, binary32 rows of 49152).
+// 4953, explicit-mask backward 5332 vs 4044); at NV = 16 a row that keeps its fp32 values
+// no longer fits in the 128 registers a lane of a 16-wavefront workgroup has, and those
+// spilling kernels run 1.0-3.8x slower than the stream kernels (bfloat16 rows of 98304,
+// binary32 rows of 49152).
 constexpr int kAutoMaxNV = 8;
+// The same cap for the forward of the tril and band masks on rows of 16-byte vectors, whose
+// row parts at 16 vectors keep raw vectors only (RowPart's RAW mode): 256 KB of a row, no
+// spill. bfloat16 rows of 100000 ran at 5799 GB/s this way against 4521-4750 on the stream
+// path. The explicit mask's and the backward's row parts still spill at 16.
+constexpr int kAutoMaxNVRaw = 16;
 constexpr int kWaveWPB = 4;     // wavefronts per workgroup on the wave path
 constexpr int kMaxW = 16;       // wavefronts per workgroup on the block path, at most
 constexpr int kStreamW = 8;     // wavefronts per workgroup on the stream path

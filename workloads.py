@@ -67,6 +67,10 @@ WORKLOADS = {
     # wavefronts of eight 16-byte vectors per lane; 34 GB per tensor
     "long_bf16_2x2x65536": Workload("long_bf16_2x2x65536", 2, 2, 65536, BF16, 1.0, 0.125,
                                     fixed_lens=(65536, 40000), x_seed=1006, len_seed=2006),
+    # rows of 200 KB (100000 bfloat16), beyond the block path's registers: the two-pass
+    # paths (the row held on chip between the passes, or streamed twice); 20 GB per plane
+    "long_bf16_2x1x100000": Workload("long_bf16_2x1x100000", 2, 1, 100000, BF16, 1.0, 0.125,
+                                     fixed_lens=(100000, 70000), x_seed=1007, len_seed=2007),
 }
 
 
