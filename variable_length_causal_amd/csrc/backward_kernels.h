@@ -119,18 +119,21 @@ __device__ __forceinline__ void bwd_wave_row(const FwdArgs& a, uint32_t plane, i
     const rsrc_t out = make_rsrc(sp.out, sp.out_bytes);
     const Cols k = kept_cols<MK>(a, r, L);
     if (k.empty()) {
-        write_zero_slots<IO, 0, NV, kWave, SP>(out, lane);
+        if (MK == MK_BAND && (a.flags & F_IVREL)) write_zeros_span<IO, SP>(sp, out, lane, kWave);
+        else write_zero_slots<IO, 0, NV, kWave, SP>(out, lane);
         return;
     }
     const int nin = k.c1 / IO::VEC + 1;
     const GradRows in = grad_rows<IO, MK>(a, plane, r, nin);
-    const int hv = sp.hv;
-    with_live_slots<NV>((nin + hv + kWave - 1) / kWave, [&]<int NA>() {
+    const IvRel iv = iv_layout<IO, MK>(a, sp, k, nin, out);
+    const int hv = iv.shift;
+    with_live_slots<NV>((iv.live + kWave - 1) / kWave, [&]<int NA>() {
         GradPart<IO, NA, kWave, MK, NV * IO::VEC >= kLeanElems> p;
         p.load(in.y, in.g, in.m, lane, hv, k);
-        write_zero_slots<IO, NA, NV, kWave, SP>(out, lane);
+        if (MK == MK_BAND && (a.flags & F_IVREL)) write_zeros_outside<IO, SP>(sp, out, iv, lane, kWave);
+        else write_zero_slots<IO, NA, NV, kWave, SP>(out, lane);
         p.dot(lane, hv, k);
-        p.template write<SP>(out, lane, hv, k, a.k, wave_reduce<OpSum>(p.d));
+        p.template write<SP>(iv.out, lane, hv, k, a.k, wave_reduce<OpSum>(p.d));
     });
 }
 
@@ -160,17 +163,20 @@ __device__ __forceinline__ void bwd_block_row(const FwdArgs& a, uint32_t plane, 
     const rsrc_t out = make_rsrc(sp.out, sp.out_bytes);
     const Cols k = kept_cols<MK>(a, r, L);
     if (k.empty()) {
-        write_zero_slots<IO, 0, NV, T, SP>(out, t);
+        if (MK == MK_BAND && (a.flags & F_IVREL)) write_zeros_span<IO, SP>(sp, out, t, T);
+        else write_zero_slots<IO, 0, NV, T, SP>(out, t);
         return;
     }
     const int wave = uniform(t / kWave);
     const int nin = k.c1 / IO::VEC + 1;
     const GradRows in = grad_rows<IO, MK>(a, plane, r, nin);
-    const int hv = sp.hv;
-    with_live_slots<NV>((nin + hv + T - 1) / T, [&]<int NA>() {
+    const IvRel iv = iv_layout<IO, MK>(a, sp, k, nin, out);
+    const int hv = iv.shift;
+    with_live_slots<NV>((iv.live + T - 1) / T, [&]<int NA>() {
         GradPart<IO, NA, T, MK, NV * IO::VEC >= kLeanElems> p;
         p.load(in.y, in.g, in.m, t, hv, k);
-        write_zero_slots<IO, NA, NV, T, SP>(out, t);
+        if (MK == MK_BAND && (a.flags & F_IVREL)) write_zeros_outside<IO, SP>(sp, out, iv, t, T);
+        else write_zero_slots<IO, NA, NV, T, SP>(out, t);
         p.dot(t, hv, k);
         const float dw = wave_reduce<OpSum>(p.d);
         if ((t & (kWave - 1)) == 0) pd[wave] = dw;
@@ -178,7 +184,7 @@ __device__ __forceinline__ void bwd_block_row(const FwdArgs& a, uint32_t plane, 
         float D = 0.0f;
 #pragma unroll
         for (int w = 0; w < W; ++w) D += pd[w];
-        p.template write<SP>(out, t, hv, k, a.k, D);
+        p.template write<SP>(iv.out, t, hv, k, a.k, D);
     });
 }
 

@@ -51,7 +51,7 @@
 
 namespace gtms {
 
-enum : unsigned { F_PAIR = 1u, F_XCD = 2u, F_LINES = 4u };
+enum : unsigned { F_PAIR = 1u, F_XCD = 2u, F_LINES = 4u, F_IVREL = 8u };
 enum : int { MK_TRIL = 0, MK_BAND = 1, MK_MASK = 2 };
 
 
@@ -190,6 +190,58 @@ __device__ __forceinline__ Span row_span(const FwdArgs& a, uint32_t plane, int r
     }
     if (tail && !last && !tail_zone_has_data<MK>(a, r, L, tail, ESIZE)) sp.out_bytes -= tail;
     return sp;
+}
+
+// ------------------------------------------------------------- narrow bands (F_IVREL)
+// A band narrower than the row keeps only its interval's vectors in registers: slot j of
+// thread t holds the natural vector v0 + t + j*STRIDE, v0 the first vector of the interval's
+// first 128-byte line, so that the row parts run with the shift -v0, and everything outside
+// those lines is plain zero stores. The host picks the kernel from the interval's width instead of S: a
+// 512-column causal window on rows of 4096 takes one wavefront per row, without the
+// workgroup's barrier. Full-width bands keep the row-relative slots, and so the tril mask's
+// bits.
+struct IvRel {
+    int shift;   // the row parts' slot shift: -v0 (interval-relative) or the span's hv
+    int live;    // vectors the row parts hold
+    rsrc_t out;  // where the row parts write: the interval's vectors, or the whole span
+};
+
+template <class IO, int MK>
+__device__ __forceinline__ IvRel iv_layout(const FwdArgs& a, const Span& sp, const Cols& k,
+                                           int nin, rsrc_t span_out) {
+    if (MK == MK_BAND && (a.flags & F_IVREL)) {
+        // The held region is the interval widened to whole 128-byte lines inside the span, so
+        // that no line is written in two parts at two times (the zero stores early, the data
+        // late); its vectors before c0 and after c1 are written as zeros with the data.
+        const int nspan = (int)(sp.out_bytes / IO::BYTES);
+        const uintptr_t base = (uintptr_t)sp.out;
+        const uintptr_t first = (base + (uintptr_t)(k.c0 / IO::VEC + sp.hv) * IO::BYTES) & ~uintptr_t(127);
+        const uintptr_t last = (base + (uintptr_t)(nin + sp.hv) * IO::BYTES + 127) & ~uintptr_t(127);
+        const int s0 = first <= base ? 0 : (int)((first - base) / IO::BYTES);
+        const int s1 = min(nspan, (int)((last - base) / IO::BYTES));
+        return {sp.hv - s0, s1 - s0,
+                make_rsrc(sp.out + s0 * IO::BYTES, (uint32_t)((s1 - s0) * IO::BYTES))};
+    }
+    return {sp.hv, nin + sp.hv, span_out};
+}
+
+// Interval-relative rows: zeros into the whole span (a row with nothing kept: the kernel's
+// slots are sized for the interval, not the row), thread t of T taking every T-th slot.
+template <class IO, int SP>
+__device__ __forceinline__ void write_zeros_span(const Span& sp, rsrc_t out, int t, int T) {
+    const int nspan = (int)(sp.out_bytes / IO::BYTES);
+    for (int s = t; s < nspan; s += T) IO::template store<SP>(out, s * IO::BYTES, IO::zero());
+}
+
+// Interval-relative rows: zeros into the span's slots before and after the held region (slots
+// [sp.hv - shift, sp.hv - shift + live)), thread t of T taking every T-th slot.
+template <class IO, int SP>
+__device__ __forceinline__ void write_zeros_outside(const Span& sp, rsrc_t out, const IvRel& iv,
+                                                    int t, int T) {
+    const int nspan = (int)(sp.out_bytes / IO::BYTES);
+    const int a = sp.hv - iv.shift, b = a + iv.live;
+    for (int s = t; s < a; s += T) IO::template store<SP>(out, s * IO::BYTES, IO::zero());
+    for (int s = b + t; s < nspan; s += T) IO::template store<SP>(out, s * IO::BYTES, IO::zero());
 }
 
 // ------------------------------------------------------------ one row, NA live slots
@@ -478,22 +530,25 @@ __device__ __forceinline__ void wave_row(const FwdArgs& a, uint32_t plane, int r
     const rsrc_t out = make_rsrc(sp.out, sp.out_bytes);
     const Cols k = kept_cols<MK>(a, r, L);
     if (k.empty()) {
-        write_zero_slots<IO, 0, NV, kWave, SP>(out, lane);
+        if (MK == MK_BAND && (a.flags & F_IVREL)) write_zeros_span<IO, SP>(sp, out, lane, kWave);
+        else write_zero_slots<IO, 0, NV, kWave, SP>(out, lane);
         return;
     }
     const int nin = k.c1 / IO::VEC + 1;  // natural vectors holding columns 0..c1
     const rsrc_t in = make_rsrc(row_ptr(a.x, plane, r, a), (uint32_t)(nin * IO::BYTES));
     const rsrc_t min = MK == MK_MASK ? make_rsrc(mask_row(a, plane, r), (uint32_t)(nin * IO::VEC))
                                      : in;
-    const int hv = sp.hv;
-    with_live_slots<NV>((nin + hv + kWave - 1) / kWave, [&]<int NA>() {
+    const IvRel iv = iv_layout<IO, MK>(a, sp, k, nin, out);
+    const int hv = iv.shift;
+    with_live_slots<NV>((iv.live + kWave - 1) / kWave, [&]<int NA>() {
         RowPart<IO, NA, kWave, MK, NV * IO::VEC >= kLeanElems, NA >= kRawNV> p;
         p.load(in, min, lane, hv, k);
-        write_zero_slots<IO, NA, NV, kWave, SP>(out, lane);
+        if (MK == MK_BAND && (a.flags & F_IVREL)) write_zeros_outside<IO, SP>(sp, out, iv, lane, kWave);
+        else write_zero_slots<IO, NA, NV, kWave, SP>(out, lane);
         p.compute(lane, hv, k, a.k);
         const float M = wave_reduce<OpMax>(p.m);
         const float S = wave_reduce<OpSum>(p.sum_at(M));
-        p.template write<SP>(out, lane, hv, k, p.gain(M, S));
+        p.template write<SP>(iv.out, lane, hv, k, p.gain(M, S));
     });
 }
 
@@ -549,7 +604,8 @@ __device__ __forceinline__ void block_row(const FwdArgs& a, uint32_t plane, int 
     const rsrc_t out = make_rsrc(sp.out, sp.out_bytes);
     const Cols k = kept_cols<MK>(a, r, L);
     if (k.empty()) {  // uniform over the workgroup
-        write_zero_slots<IO, 0, NV, T, SP>(out, t);
+        if (MK == MK_BAND && (a.flags & F_IVREL)) write_zeros_span<IO, SP>(sp, out, t, T);
+        else write_zero_slots<IO, 0, NV, T, SP>(out, t);
         return;
     }
     const int wave = uniform(t / kWave);
@@ -557,11 +613,13 @@ __device__ __forceinline__ void block_row(const FwdArgs& a, uint32_t plane, int 
     const rsrc_t in = make_rsrc(row_ptr(a.x, plane, r, a), (uint32_t)(nin * IO::BYTES));
     const rsrc_t min = MK == MK_MASK ? make_rsrc(mask_row(a, plane, r), (uint32_t)(nin * IO::VEC))
                                      : in;
-    const int hv = sp.hv;
-    with_live_slots<NV>((nin + hv + T - 1) / T, [&]<int NA>() {
+    const IvRel iv = iv_layout<IO, MK>(a, sp, k, nin, out);
+    const int hv = iv.shift;
+    with_live_slots<NV>((iv.live + T - 1) / T, [&]<int NA>() {
         RowPart<IO, NA, T, MK, NV * IO::VEC >= kLeanElems, NA >= kRawNV> p;
         p.load(in, min, t, hv, k);
-        write_zero_slots<IO, NA, NV, T, SP>(out, t);
+        if (MK == MK_BAND && (a.flags & F_IVREL)) write_zeros_outside<IO, SP>(sp, out, iv, t, T);
+        else write_zero_slots<IO, NA, NV, T, SP>(out, t);
         p.compute(t, hv, k, a.k);
         // wave partials, then the workgroup merge through LDS
         const float mw = wave_reduce<OpMax>(p.m);
@@ -573,7 +631,7 @@ __device__ __forceinline__ void block_row(const FwdArgs& a, uint32_t plane, int 
         __syncthreads();
         float M, S;
         merge_partials<W>(pm, ps, M, S);
-        p.template write<SP>(out, t, hv, k, p.gain(M, S));
+        p.template write<SP>(iv.out, t, hv, k, p.gain(M, S));
     });
 }
 

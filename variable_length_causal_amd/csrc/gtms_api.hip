@@ -66,17 +66,15 @@ int64_t line_slack(bool lines, int64_t row_bytes, const void* out) {
 }
 
 // Kernel choice. A lane holds NV vectors (16 bytes each on rows whose byte length is a
-// multiple of 16, else one element); a row takes 64 * W * NV slots, counting the slots it
-// may write for its predecessor (line_slack).
+// multiple of 16, else one element); a row takes 64 * W * NV slots: the vectors it may span,
+// counting those it may write for its predecessor (line_slack), or for a narrow band only its
+// interval's vectors (the rest are plain zero stores).
 //   auto:   rows up to 256 slots -> one wavefront per row (NV <= 4); longer rows -> W
 //           wavefronts per row with NV = 4 (the stores of each instruction then cover
 //           W KB of the row); W = 16 and NV up to auto_max_nv beyond that; the stream path
 //           last.
 //   forced: the named path if it can hold the row.
-int make_plan(int64_t S, int dtype, bool wide, int64_t slack, int path, int64_t auto_max_nv,
-              Plan* p) {
-    const int64_t vec = wide ? 16 / esize_of(dtype) : 1;
-    const int64_t slots = cdiv(S, vec) + slack;  // vectors a row may span
+int make_plan(int64_t slots, bool wide, int path, int64_t auto_max_nv, Plan* p) {
     p->wide = wide;
     if (path == GTMS_PATH_AUTO) {
         if (slots <= kWave * kAutoNV) path = GTMS_PATH_WAVE;
@@ -157,7 +155,20 @@ int run_impl(const void* x, const void* g, void* out, const int32_t* seq_lens, i
     // computed masks (their row parts keep raw vectors only, see RowPart), 8 otherwise
     const int64_t auto_max_nv =
         OP == OP_FWD && mk.kind != MK_MASK && wide ? kAutoMaxNVRaw : kAutoMaxNV;
-    st = make_plan(S, dtype, wide, line_slack(lines, row_bytes, out), path, auto_max_nv, &plan);
+    // A band narrower than the row holds only its interval in registers (F_IVREL), widened to
+    // whole 128-byte lines: at most ceil(width / VEC) + 1 vectors (the interval need not start
+    // on a vector boundary) plus up to a line less one vector at each end.
+    const int64_t vecn = wide ? vec : 1;
+    const int64_t per_line = 128 / (wide ? 16 : esize_of(dtype));
+    const int64_t band_width = mk.kind == MK_BAND
+        ? (mk.hi < S - 1 ? mk.hi : S - 1) - (mk.lo > -(S - 1) ? mk.lo : -(S - 1)) + 1
+        : S;
+    const int64_t iv_slots =
+        (band_width <= 0 ? 1 : cdiv(band_width, vecn) + (vecn > 1)) + 2 * (per_line - 1);
+    const int64_t row_slots = cdiv(S, vecn) + line_slack(lines, row_bytes, out);
+    const bool ivrel = mk.kind == MK_BAND && band_width < S && iv_slots < row_slots;
+    const int64_t slots = ivrel ? iv_slots : row_slots;
+    st = make_plan(slots, wide, path, auto_max_nv, &plan);
     if (st != GTMS_OK) return st;
 
     FwdArgs a;
@@ -173,6 +184,7 @@ int run_impl(const void* x, const void* g, void* out, const int32_t* seq_lens, i
     if (!(flags & GTMS_FLAG_PLAIN_ORDER)) a.flags |= F_XCD;
     a.xcd_shift = kXcdChunkLog2;
     if (lines && plan.path != GTMS_PATH_STREAM) a.flags |= F_LINES;
+    if (ivrel) a.flags |= F_IVREL;
     a.units_per_plane = (a.flags & F_PAIR) ? (uint32_t)((S + 1) / 2) : (uint32_t)S;
     const int64_t units = B * M * (int64_t)a.units_per_plane;
     if (units > (int64_t)UINT32_MAX || B * M > (int64_t)UINT32_MAX) return GTMS_ERR_INVALID_ARG;
