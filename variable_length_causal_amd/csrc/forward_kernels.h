@@ -308,7 +308,10 @@ struct RowPart {
         for (int j = 0; j < NA; ++j) {
             const int v = t + j * STRIDE - hv;
             const bool skip = v < v0;
-            raw[j] = IO::template load<kPolicyDefault>(in, skip ? kOutOfRange : v * IO::BYTES);
+            // an explicit mask's scores stream past (non-temporal), so that the mask rows the
+            // planes share stay in L2
+            raw[j] = IO::template load<MK == MK_MASK ? kPolicyReadOnce : kPolicyDefault>(
+                in, skip ? kOutOfRange : v * IO::BYTES);
             if constexpr (MK == MK_MASK)
                 mk[j] = MIO::load(min, skip ? kOutOfRange : v * IO::VEC);
         }
