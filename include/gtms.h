@@ -76,7 +76,12 @@ enum gtms_path {
                              rows up to 1024 vectors (4096 binary32 / 8192 16-bit
                              elements on aligned rows) */
     GTMS_PATH_BLOCK = 2,  /* one workgroup of 2-16 wavefronts per row, per-wave (max, sum)
-                             partials merged through LDS: rows up to 16384 vectors */
+                             partials merged through LDS: rows up to 16384 vectors. The
+                             backward of the computed masks on 16-byte vectors holds rows
+                             past 8192 vectors as 8192 in registers and up to 5056 more of
+                             y and dy in LDS (16-bit rows up to 105984 elements, binary32
+                             up to 52992); longer rows there use 16 vectors per lane in
+                             registers */
     GTMS_PATH_STREAM = 3  /* one workgroup per row, two passes over the row: online
                              (max, sum), then normalise (any row length) */
 };

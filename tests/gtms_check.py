@@ -146,19 +146,46 @@ def check_planes_against_oracle(x_dev, y_dev, lens, scale: float, dtype: int,
 
 
 def oracle_forward_to_device(x_dev, lens, scale: float, dtype: int,
-                             chunk_bytes: int = 4 << 30):
+                             chunk_bytes: int = 4 << 30, rows_per_call: int = 512):
     """The oracle's forward of a [B, M, S, S] device tensor, rounded into the element type and
-    returned as a new device tensor: planes go to the host in chunks of at most chunk_bytes,
-    one oracle call per plane on host threads, and the rounded planes are copied back. Lets a
-    full-size backward run on real softmax rows that do not come from the GPU path."""
+    returned as a new device tensor. Planes that fit a host chunk (chunk_bytes for x and y
+    together) go to the host a chunk at a time, one oracle call per plane on host threads, and
+    come back rounded by the oracle. Larger planes go through the oracle's row entry point in
+    blocks of rows_per_call rows on host threads; its fp64 rows are rounded to the element
+    type through binary32 (for 16-bit types this differs from one rounding only at rare
+    ties; the rows are inputs, and each test's reference takes them as they are). Lets a
+    full-size backward run on real softmax rows that do not come from the GPU path. Prints
+    its progress on large planes."""
     import oracle
     import torch
 
     B, M, S, _ = x_dev.shape
-    xf = x_dev.reshape(B * M, S, S)
     y_dev = torch.empty_like(x_dev)
+    per_chunk = chunk_bytes // (2 * S * S * esize(dtype))
+    if per_chunk < 1:
+        tasks = [(b, m, r0) for b in range(B) for m in range(M)
+                 for r0 in range(0, S, rows_per_call)]
+        done = [0]
+
+        def rows(task):
+            b, m, r0 = task
+            r1 = min(S, r0 + rows_per_call)
+            xs = workloads.to_storage(x_dev[b, m, r0:r1].cpu())
+            ref = oracle.softmax_rows_f64(xs, np.arange(r0, r1), [lens[b]] * (r1 - r0), scale,
+                                          dtype)
+            y_dev[b, m, r0:r1].copy_(
+                torch.from_numpy(ref).to(torch.float32).to(workloads.torch_dtype(dtype)))
+            done[0] += 1
+            if done[0] % max(1, len(tasks) // 10) == 0:
+                print(f"oracle forward: {done[0]} of {len(tasks)} row blocks", flush=True)
+
+        with ThreadPoolExecutor(max_workers=host_threads()) as pool:
+            list(pool.map(rows, tasks))
+        if y_dev.is_cuda:
+            torch.cuda.synchronize()
+        return y_dev
+    xf = x_dev.reshape(B * M, S, S)
     yf = y_dev.reshape(B * M, S, S)
-    per_chunk = max(1, chunk_bytes // (2 * S * S * esize(dtype)))
     with ThreadPoolExecutor(max_workers=host_threads()) as pool:
         for p0 in range(0, B * M, per_chunk):
             p1 = min(B * M, p0 + per_chunk)
@@ -240,6 +267,22 @@ def check_planes_backward_against_oracle(y_dev, dy_dev, dx_dev, lens, scale: flo
     return worst
 
 
+def _run_blocks(one, tasks, what: str = "rows checked") -> float:
+    """Runs one(task) on host threads and returns the max of the results, printing progress
+    every tenth of the tasks (long checks must not run silently)."""
+    done = [0]
+
+    def step(task):
+        e = one(task)
+        done[0] += 1
+        if len(tasks) >= 50 and done[0] % (len(tasks) // 10) == 0:
+            print(f"{what}: {done[0]} of {len(tasks)} blocks", flush=True)
+        return e
+
+    with ThreadPoolExecutor(max_workers=host_threads()) as pool:
+        return max([0.0] + list(pool.map(step, tasks)))
+
+
 def check_rows_against_oracle(x_dev, y_dev, lens, scale: float, dtype: int,
                               tol: float | None = None, rows_per_call: int = 1024) -> float:
     """Every element of a [B, M, S, S] forward result on the device, for planes too large to
@@ -271,8 +314,7 @@ def check_rows_against_oracle(x_dev, y_dev, lens, scale: float, dtype: int,
         assert e <= tol, f"b={b} m={m} rows {r0}..{r1}: max error {e:.3g} > {tol:.3g}"
         return e
 
-    with ThreadPoolExecutor(max_workers=host_threads()) as pool:
-        return max([0.0] + list(pool.map(one, tasks)))
+    return _run_blocks(one, tasks)
 
 
 def check_rows_backward_against_oracle(y_dev, dy_dev, dx_dev, lens, scale: float, dtype: int,
@@ -309,5 +351,4 @@ def check_rows_backward_against_oracle(y_dev, dy_dev, dx_dev, lens, scale: float
         assert not bad.any(), f"b={b} m={m} rows {r0}..{r1}: {int(bad.sum())} kept elements beyond the bound"
         return float(np.max(np.where(keep, err, 0.0)))
 
-    with ThreadPoolExecutor(max_workers=host_threads()) as pool:
-        return max([0.0] + list(pool.map(one, tasks)))
+    return _run_blocks(one, tasks)

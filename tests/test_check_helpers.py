@@ -127,3 +127,16 @@ def test_oracle_forward_to_device(dtype):
     assert y.dtype == x.dtype and tuple(y.shape) == tuple(x.shape)
     got = workloads.to_storage(y)
     assert np.array_equal(got.view(np.uint8), whole.view(np.uint8))
+    # planes larger than a chunk: blocks of rows through the row entry point, rounded through
+    # binary32 (the same values here except at rare ties of the 16-bit rounding)
+    yr = oracle_forward_to_device(x, lens, 0.7, dtype, chunk_bytes=1000, rows_per_call=7)
+    assert yr.dtype == x.dtype and tuple(yr.shape) == tuple(x.shape)
+    got_r = workloads.to_storage(yr)
+    ref = oracle.softmax_f64(workloads.to_storage(x), lens, 0.7, dtype)
+    if dtype == workloads.F32:
+        assert np.array_equal(got_r.view(np.uint8), whole.view(np.uint8))
+    else:
+        # within half an ulp of the 16-bit type plus the binary32 step, and masked cells +0
+        from gtms_check import bits, to_f64
+        assert not bits(got_r)[ref == 0].any()
+        assert np.max(np.abs(to_f64(got_r, dtype) - ref)) <= 2.0 ** -8 * max(1.0, np.max(ref))

@@ -245,3 +245,70 @@ def test_backward_full_long_rows():
     print(f"{w.name}: every element of the backward checked, worst error {worst:.3g}", flush=True)
     del y, dy, dx
     torch.cuda.empty_cache()
+
+
+def test_backward_full_long_bf16_2x1x100000():
+    """The 100000-wide-row workload (bf16 2 x 1 x 100000, lengths 100000 and 70000) at full
+    size on real softmax rows: y is the oracle's rounded forward of the workload's own seeded
+    scores, dy normal. Rows whose kept prefix passes 65536 elements keep 8 vectors per lane in
+    registers and the rest of y and dy in LDS; shorter rows of the same launch fit the
+    registers, rows at or past the length are zeros. Every element against the oracle's
+    backward row entry point; the forced block path (the same kernel) and the band [-S, 0]
+    (the same kept set) give the same bits."""
+    w = workloads.WORKLOADS["long_bf16_2x1x100000"]
+    lens = workloads.seq_lens(w)
+    print(f"backward full workload {w.name} lens={list(lens)}", flush=True)
+    x = workloads.scores_device(w.shape, w.dtype, w.sigma, w.x_seed)
+    y = oracle_forward_to_device(x, lens, w.scale, w.dtype)
+    del x
+    torch.cuda.empty_cache()
+    dy = workloads.scores_device(w.shape, w.dtype, 1.0, 4246)
+    sl = torch.as_tensor(lens).cuda()
+    dx = g.backward(y, dy, sl, w.scale)
+    torch.cuda.synchronize()
+    worst = check_rows_backward_against_oracle(y, dy, dx, lens, w.scale, w.dtype, U[w.dtype],
+                                               TINY[w.dtype])
+    print(f"{w.name}: every element of the backward checked, worst error {worst:.3g}", flush=True)
+    for tag, run in (("block", lambda: g.backward(y, dy, sl, w.scale, path="block")),
+                     ("band [-S, 0]", lambda: g.backward_band(y, dy, sl, -w.S, 0, w.scale))):
+        other = run()
+        torch.cuda.synchronize()
+        assert torch.equal(other.view(torch.int16), dx.view(torch.int16)), tag
+        del other
+    del y, dy, dx
+    torch.cuda.empty_cache()
+
+
+def test_backward_stash_rows():
+    """Rows past 8 vectors per lane that the LDS stash takes: binary32 rows of 40000 (10000
+    vectors, 8192 of them in registers), and a bfloat16 causal window of 70001 columns on rows
+    of 100000, whose rows hold only their interval (up to 8766 vectors). y is uniform in
+    [0, 2/n) over the kept set (n its width) and zero elsewhere, dy normal. With y zero
+    outside the window, D and every kept dx of the window equal those of the grouped tril
+    mask, so every element compares with the oracle's tril backward rows; the window's
+    masked elements must also be +0 bit for bit."""
+    cases = ((workloads.F32, 40000, 40000 - 3, None, 0.7),
+             (workloads.BF16, 100000, 100000 - 5, -70000, 0.3))
+    for dtype, S, L, lo, scale in cases:
+        print(f"backward stash rows S={S} dtype={DNAME[dtype]} L={L} lo={lo}", flush=True)
+        n = L if lo is None else -lo + 1
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(S + 7)
+        y = torch.rand((1, 1, S, S), generator=gen, device="cuda").mul_(2.0 / n).to(
+            workloads.torch_dtype(dtype))
+        if lo is not None:
+            y.triu_(lo)
+        dy = workloads.scores_device((1, 1, S, S), dtype, 1.0, S + 8)
+        sl = torch.as_tensor(np.asarray([L], dtype=np.int32)).cuda()
+        dx = (g.backward(y, dy, sl, scale) if lo is None
+              else g.backward_band(y, dy, sl, lo, 0, scale))
+        torch.cuda.synchronize()
+        lens = np.asarray([L], np.int32)
+        worst = check_rows_backward_against_oracle(y, dy, dx, lens, scale, dtype, U[dtype],
+                                                   TINY[dtype])
+        if lo is not None:
+            ib = torch.int32 if dtype == workloads.F32 else torch.int16
+            assert torch.equal(dx.triu(lo).view(ib), dx.view(ib)), "window: masked bits set"
+        print(f"S={S}: every element checked, worst error {worst:.3g}", flush=True)
+        del y, dy, dx
+        torch.cuda.empty_cache()

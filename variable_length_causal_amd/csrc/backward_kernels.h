@@ -202,6 +202,148 @@ __global__ __launch_bounds__(W * kWave) void bwd_block(FwdArgs a) {
     }
 }
 
+// --------------------------------------------------------------------------- bwd_stash
+// Rows past 8 vectors per lane of a 16-wavefront workgroup (16-bit rows of more than 65536
+// elements, binary32 rows of more than 32768), for the computed masks on rows of 16-byte
+// vectors. Both passes need y and g, 32 bytes per vector position, and a lane of such a
+// workgroup has 128 registers: at 16 vectors per lane bwd_block's row part spills. So each
+// lane keeps 8 slots in registers (bwd_block's GradPart) and the row's further vectors, up to
+// kStashVecs of each of y and g, go to LDS. The buffer unit writes them there itself (loads
+// with the LDS flag: lane l's 16 bytes land at the wavefront's base + 16 l, a lane whose
+// offset fails the range check writes zeros), so they take no registers. Stash entry
+// i = n * T + t (slot NV + n of thread t) is filled by thread t's own load and read only by
+// thread t, so a wait for the thread's own loads orders them, and the next row's loads
+// follow this row's reads in program order. Every element of y and g crosses HBM once, as
+// on the block path; the stream path reads both twice.
+constexpr int kStashVecs = 5056;  // 2 x 5056 x 16 = 161792 bytes of the 160 KiB of LDS
+static_assert(kStashVecs % kWave == 0, "each wavefront fills whole 1 KiB blocks");
+
+// Zeros into the span's slots [from, end of span), thread t of T taking every T-th slot.
+template <class IO, int SP>
+__device__ __forceinline__ void write_zeros_from(const Span& sp, rsrc_t out, int from, int t,
+                                                 int T) {
+    const int nspan = (int)(sp.out_bytes / IO::BYTES);
+    for (int s = from + t; s < nspan; s += T) IO::template store<SP>(out, s * IO::BYTES, IO::zero());
+}
+
+template <int DT, int NV, int W, int SP, int MK>
+__device__ __forceinline__ void bwd_stash_row(const FwdArgs& a, uint32_t plane, int r, int L,
+                                              float* pd, u32x4* ys, u32x4* gs) {
+    using IO = Io<DT, true>;
+    constexpr int T = W * kWave;
+    constexpr int VEC = IO::VEC;
+    constexpr bool LEAN = NV * VEC >= kLeanElems;
+    constexpr int NSL = (kStashVecs + T - 1) / T;  // stash slots per thread, at most
+    static_assert(MK != MK_MASK, "the explicit mask's bytes have no stash");
+    const int t = threadIdx.x, lane = t & (kWave - 1);
+    const Span sp = row_span<MK, IO::BYTES / VEC>(a, plane, r, L);
+    const rsrc_t out = make_rsrc(sp.out, sp.out_bytes);
+    const Cols k = kept_cols<MK>(a, r, L);
+    if (k.empty()) {
+        write_zeros_span<IO, SP>(sp, out, t, T);
+        return;
+    }
+    const int wave = uniform(t / kWave);
+    const int nin = k.c1 / VEC + 1;
+    const GradRows in = grad_rows<IO, MK>(a, plane, r, nin);
+    const IvRel iv = iv_layout<IO, MK>(a, sp, k, nin, out);
+    const bool ivrel = MK == MK_BAND && (a.flags & F_IVREL);
+    const int hv = iv.shift;
+    auto merge = [&](float d) {
+        const float dw = wave_reduce<OpSum>(d);
+        if (lane == 0) pd[wave] = dw;
+        __syncthreads();
+        float D = 0.0f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) D += pd[w];
+        return D;
+    };
+    if (iv.live <= NV * T) {  // uniform: the row fits the registers (bwd_block's row)
+        with_live_slots<NV>((iv.live + T - 1) / T, [&]<int NA>() {
+            GradPart<IO, NA, T, MK, LEAN> p;
+            p.load(in.y, in.g, in.m, t, hv, k);
+            if (ivrel) write_zeros_outside<IO, SP>(sp, out, iv, t, T);
+            else write_zeros_from<IO, SP>(sp, out, NA * T, t, T);
+            p.dot(t, hv, k);
+            p.template write<SP>(iv.out, t, hv, k, a.k, merge(p.d));
+        });
+        return;
+    }
+    // Slots NV and up live in LDS: the held positions [NV*T, live) of the row part, at most
+    // kStashVecs of them (the host's choice of this kernel guarantees it).
+    using GP = GradPart<IO, NV, T, MK, LEAN>;
+    const int nst = iv.live - NV * T;
+    const int v0 = MK == MK_TRIL ? 0 : k.c0 / VEC;
+#pragma unroll
+    for (int n = 0; n < NSL; ++n) {
+        const int base = n * T + wave * kWave;  // the wavefront's first entry of this slot
+        if (base < nst) {                       // uniform; base + 64 <= nst rounded up <= kStashVecs
+            const int i = base + lane, v = NV * T + i - hv;
+            const int off = i >= nst || v < v0 ? kOutOfRange : v * IO::BYTES;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                in.y, (__attribute__((address_space(3))) void*)(ys + base), 16, off, 0, 0,
+                kPolicyReadOnce);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                in.g, (__attribute__((address_space(3))) void*)(gs + base), 16, off, 0, 0,
+                kPolicyReadOnce);
+        }
+    }
+    GP p;
+    p.load(in.y, in.g, in.m, t, hv, k);
+    if (ivrel) write_zeros_outside<IO, SP>(sp, out, iv, t, T);
+    else write_zeros_from<IO, SP>(sp, out, iv.live, t, T);
+    p.dot(t, hv, k);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's stash entries have landed
+    float d = p.d;
+#pragma unroll
+    for (int n = 0; n < NSL; ++n) {
+        const int i = n * T + t;
+        if (i < nst) {
+            const int j = NV + n;
+            const int kc = GP::kept_count(t, j, hv, k), ka = GP::kept_from(t, j, hv, k);
+            float fy[VEC], fg[VEC];
+            IO::unpack(ys[i], fy);
+            IO::unpack(gs[i], fg);
+#pragma unroll
+            for (int q = 0; q < VEC; ++q)
+                d += GP::kept(typename GP::MIO::raw_t{}, q, ka, kc) ? fy[q] * fg[q] : 0.0f;
+        }
+    }
+    const float D = merge(d);
+    p.template write<SP>(iv.out, t, hv, k, a.k, D);
+#pragma unroll
+    for (int n = 0; n < NSL; ++n) {
+        const int i = n * T + t;
+        if (i < nst) {
+            const int j = NV + n;
+            const int kc = GP::kept_count(t, j, hv, k), ka = GP::kept_from(t, j, hv, k);
+            float fy[VEC], fg[VEC], o[VEC];
+            IO::unpack(ys[i], fy);
+            IO::unpack(gs[i], fg);
+#pragma unroll
+            for (int q = 0; q < VEC; ++q)
+                o[q] = GP::kept(typename GP::MIO::raw_t{}, q, ka, kc) ? a.k * fy[q] * (fg[q] - D)
+                                                                       : 0.0f;
+            IO::template store<SP>(iv.out, (t + j * T) * IO::BYTES, IO::pack(o));
+        }
+    }
+}
+
+template <int DT, int NV, int W, int SP, int MK>
+__global__ __launch_bounds__(W * kWave) void bwd_stash(FwdArgs a) {
+    __shared__ __attribute__((aligned(16))) u32x4 ys[kStashVecs], gs[kStashVecs];
+    __shared__ float part[2][W];
+    const uint32_t nblk = gridDim.x;
+    const uint32_t blk = (a.flags & F_XCD) ? xcd_chunked(blockIdx.x, nblk, a.xcd_shift) : blockIdx.x;
+    for (uint64_t unit = blk; unit < a.n_units; unit += nblk) {
+        const Unit u = decode_unit((uint32_t)unit, a);
+        const int L = valid_len<MK>(a, u.plane);
+        bwd_stash_row<DT, NV, W, SP, MK>(a, u.plane, u.r0, L, part[0], ys, gs);
+        if (u.r1 >= 0) bwd_stash_row<DT, NV, W, SP, MK>(a, u.plane, u.r1, L, part[1], ys, gs);
+        __syncthreads();
+    }
+}
+
 // -------------------------------------------------------------------------- bwd_stream
 // Rows of any length: pass 1 accumulates D, pass 2 re-reads both intervals and writes.
 template <int DT, bool WIDE, int W, int SP, int MK>

@@ -71,14 +71,21 @@ int64_t line_slack(bool lines, int64_t row_bytes, const void* out) {
 // interval's vectors (the rest are plain zero stores).
 //   auto:   rows up to 256 slots -> one wavefront per row (NV <= 4); longer rows -> W
 //           wavefronts per row with NV = 4 (the stores of each instruction then cover
-//           W KB of the row); W = 16 and NV up to auto_max_nv beyond that; the stream path
-//           last.
-//   forced: the named path if it can hold the row.
-int make_plan(int64_t slots, bool wide, int path, int64_t auto_max_nv, Plan* p) {
+//           W KB of the row); W = 16 and NV up to auto_max_nv beyond that; then, where
+//           stash_cap > 0 (the backward of the computed masks on 16-byte vectors), W = 16
+//           with 8 vectors per lane in registers and up to stash_cap more per row in LDS;
+//           the stream path last.
+//   forced: the named path if it can hold the row (the block path at 16 vectors per lane
+//           takes the LDS stash when stash_cap > 0 and the row fits it).
+int make_plan(int64_t slots, bool wide, int path, int64_t auto_max_nv, int64_t stash_cap,
+              Plan* p) {
     p->wide = wide;
+    p->stash = false;
+    const int64_t stash_slots = int64_t(kWave) * kMaxW * kAutoMaxNV + stash_cap;
     if (path == GTMS_PATH_AUTO) {
         if (slots <= kWave * kAutoNV) path = GTMS_PATH_WAVE;
         else if (slots <= int64_t(kWave) * kMaxW * auto_max_nv) path = GTMS_PATH_BLOCK;
+        else if (stash_cap > 0 && slots <= stash_slots) path = GTMS_PATH_BLOCK;
         else path = GTMS_PATH_STREAM;
     }
     p->path = path;
@@ -96,6 +103,7 @@ int make_plan(int64_t slots, bool wide, int path, int64_t auto_max_nv, Plan* p) 
             if (nv > kMaxNV) return GTMS_ERR_PATH;
             p->w = (int)w;
             p->nv = (int)nv;
+            p->stash = stash_cap > 0 && nv > kAutoMaxNV && w == kMaxW && slots <= stash_slots;
             return GTMS_OK;
         }
         case GTMS_PATH_STREAM:
@@ -168,7 +176,9 @@ int run_impl(const void* x, const void* g, void* out, const int32_t* seq_lens, i
     const int64_t row_slots = cdiv(S, vecn) + line_slack(lines, row_bytes, out);
     const bool ivrel = mk.kind == MK_BAND && band_width < S && iv_slots < row_slots;
     const int64_t slots = ivrel ? iv_slots : row_slots;
-    st = make_plan(slots, wide, path, auto_max_nv, &plan);
+    // the backward's LDS stash holds 16-byte vectors of y and g, for the computed masks
+    const int64_t stash_cap = OP == OP_BWD && mk.kind != MK_MASK && wide ? kStashVecs : 0;
+    st = make_plan(slots, wide, path, auto_max_nv, stash_cap, &plan);
     if (st != GTMS_OK) return st;
 
     FwdArgs a;

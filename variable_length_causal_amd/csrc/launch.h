@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "attention_kernels.h"
+#include "backward_kernels.h"
 #include "forward_kernels.h"
 
 namespace gtms {
@@ -26,6 +27,9 @@ constexpr int kAutoMaxNV = 8;
 // spill. bfloat16 rows of 100000 ran at 5799 GB/s this way against 4521-4750 on the stream
 // path. The explicit mask's and the backward's row parts still spill at 16.
 constexpr int kAutoMaxNVRaw = 16;
+// The backward of the computed masks on rows of 16-byte vectors goes further on the block
+// path: rows of up to kAutoMaxNV * 1024 + kStashVecs vectors keep 8 vectors per lane in
+// registers and the rest in LDS (bwd_stash), so that y and g cross HBM once.
 constexpr int kWaveWPB = 4;     // wavefronts per workgroup on the wave path
 constexpr int kMaxW = 16;       // wavefronts per workgroup on the block path, at most
 constexpr int kStreamW = 8;     // wavefronts per workgroup on the stream path
@@ -39,6 +43,7 @@ struct Plan {
     bool wide;
     int nv;    // vectors per lane (wave, block)
     int w;     // wavefronts per row (block, stream)
+    bool stash = false;  // block path, backward: rows past 8 vectors per lane keep the rest in LDS
 };
 
 // Launches the kernel the plan names for element type `dtype` (a GTMS_* code).

@@ -38,6 +38,18 @@ hipError_t launch_block(const FwdArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// The backward's block path with 8 register slots per lane and an LDS stash (bwd_stash).
+template <int OP, int MK, int DT, bool WIDE>
+hipError_t launch_stash(const FwdArgs& a, hipStream_t st) {
+    if constexpr (OP == OP_BWD && MK != MK_MASK && WIDE) {
+        const dim3 grid(grid_for(a.n_units, 1)), block(kMaxW * kWave);
+        hipLaunchKernelGGL((bwd_stash<DT, kAutoMaxNV, kMaxW, kPolicyStream, MK>), grid, block, 0, st, a);
+        return hipGetLastError();
+    } else {
+        return hipErrorInvalidValue;
+    }
+}
+
 template <int OP, int MK, int DT, bool WIDE>
 hipError_t launch_stream(const FwdArgs& a, hipStream_t st) {
     const dim3 grid(grid_for(a.n_units, 1)), block(kStreamW * kWave);
@@ -83,7 +95,9 @@ hipError_t dispatch_wide(const Plan& p, const FwdArgs& a, hipStream_t st) {
                         case 2: return launch_block<OP, MK, DT, WIDE, 2, 16>(a, st);
                         case 4: return launch_block<OP, MK, DT, WIDE, 4, 16>(a, st);
                         case 8: return launch_block<OP, MK, DT, WIDE, 8, 16>(a, st);
-                        case 16: return launch_block<OP, MK, DT, WIDE, 16, 16>(a, st);
+                        case 16:
+                            if (p.stash) return launch_stash<OP, MK, DT, WIDE>(a, st);
+                            return launch_block<OP, MK, DT, WIDE, 16, 16>(a, st);
                         default: return hipErrorInvalidValue;
                     }
             }
