@@ -131,7 +131,7 @@ def bench_attention(args):
 
     def step(i):
         q, k, v = qkv[i % nsets]
-        g.attention(q, k, v, sl, w.scale, out=outs[i % nsets])
+        g.attention(q, k, v, sl, w.scale, out=outs[i % nsets], split=args.split)
 
     for i in range(args.warmup):
         step(i)
@@ -176,7 +176,8 @@ def bench_attention(args):
         "vs_baseline": None,
         "dtype": workloads.DTYPE_NAMES[w.dtype],
         "data": "synthetic (seeded normal q, k, v generated on the device, seeded lengths)",
-        "config": {"workload": w.name, "op": "attention", "B": w.B, "M": w.M, "S": w.S,
+        "config": {"workload": w.name, "op": "attention", "split": args.split,
+                   "B": w.B, "M": w.M, "S": w.S,
                    "D": w.D, "seq_lens": [int(v) for v in lens], "scale": w.scale,
                    "flops_per_step": flops,
                    "kernel_ms_min": round(float(np.min(kernel_ms)), 5),
@@ -371,6 +372,8 @@ def main():
                          "the window mask tril(w)")
     ap.add_argument("--path", default="auto", choices=["auto", "wave", "block", "stream"])
     ap.add_argument("--flags", type=int, default=0)
+    ap.add_argument("--split", default="auto", choices=["auto", "off", "on"],
+                    help="attention: the key split of each query tile (head size 64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--copy-calibration", action="store_true",

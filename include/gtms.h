@@ -221,6 +221,29 @@ int gtms_attention_forward(const void* q, const void* k, const void* v, void* ou
                            const int32_t* seq_lens, int64_t B, int64_t M, int64_t S, int64_t D,
                            float scale, int dtype, void* stream);
 
+/* Work split of the fused attention for gtms_attention_forward_ex. Each workgroup computes
+ * one 128-row query tile of one head; at head size 64 it can instead hold two groups of four
+ * wavefronts that take the first and second half of the tile's key blocks, each with its own
+ * running (max, sum) and accumulators, merged at the end as the split-KV reduction of
+ * flash_decoding.py does (the page "flash_decoding.py", _flash_decoding_fwd_reduce_kernel):
+ * m = max of the parts' maxima, l = sum of l_i 2^(m_i - m), out = sum of out_i 2^(m_i - m).
+ * That halves the longest chain of key blocks, which sets the launch's length when a grid
+ * has few tiles per compute unit. AUTO (what gtms_attention_forward uses) takes the split
+ * at head size 64 when S >= 2048 and the grid has at most 3 (head, tile) pairs per compute
+ * unit of the device. The two choices reduce in different orders, so they agree to within
+ * rounding. */
+enum gtms_attn_split {
+    GTMS_ATTN_SPLIT_AUTO = 0,
+    GTMS_ATTN_SPLIT_OFF = 1,
+    GTMS_ATTN_SPLIT_ON = 2  /* head size 64 only; at 128 the choice is ignored */
+};
+
+/* gtms_attention_forward with an explicit work split (a GTMS_ATTN_SPLIT_* value; others give
+ * GTMS_ERR_PATH). Meant for tests and tuning. */
+int gtms_attention_forward_ex(const void* q, const void* k, const void* v, void* out,
+                              const int32_t* seq_lens, int64_t B, int64_t M, int64_t S,
+                              int64_t D, float scale, int dtype, int split, void* stream);
+
 /* A static, human-readable description of a status code. */
 const char* gtms_status_string(int status);
 

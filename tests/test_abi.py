@@ -127,3 +127,22 @@ def test_variant_argument_checks(lib):
     assert lib.gtms_backward_masked(X, G, DX, 0, 0, 0, 8, SL, 1, 1, 8, 1.0, 0, 0, 0, None) == 1
     assert lib.gtms_backward_masked(X, G, DX, MK, 0, -1, 8, SL, 1, 1, 8, 1.0, 0, 0, 0, None) == 1
     assert lib.gtms_backward_masked(X, G, DX, MK, 0, 0, 8, 0, 1, 1, 8, 1.0, 0, 9, 0, None) == 5
+
+
+def test_attention_argument_checks(lib):
+    """Every call here is rejected (or is a no-op) before anything reaches the GPU."""
+    Q, K, V, O, SL = FAKE, FAKE * 2, FAKE * 4, FAKE * 8, FAKE * 16
+
+    def attn(q=Q, k=K, v=V, o=O, sl=SL, B=1, M=1, S=8, D=64, dtype=2, split=0):
+        return lib.gtms_attention_forward_ex(q, k, v, o, sl, B, M, S, D, 0.125, dtype, split,
+                                             None)
+    assert attn(dtype=0) == 2                            # binary32 is not an attention type
+    assert attn(split=3) == 5 and attn(split=-1) == 5    # unknown work split
+    assert attn(B=0, q=0, k=0, v=0, o=0, sl=0) == 0      # empty: no-op, nothing checked
+    assert attn(D=96) == 5                               # head sizes 64 and 128 only
+    assert attn(q=0) == 1 and attn(sl=0) == 1            # null pointers
+    assert attn(v=V + 8) == 3                            # 16-byte alignment
+    assert attn(o=Q + 64) == 1                           # out overlaps q
+    assert attn(S=(1 << 24) - 64) == 1                   # one head's offsets past 2^31
+    assert attn(B=-1) == 1
+    assert lib.gtms_attention_forward(Q, K, V, O, SL, 1, 1, 8, 64, 0.125, 0, None) == 2

@@ -56,14 +56,15 @@ def check_rows(o_st, ref, vmax_rows, lens_rows, rows_r, S, dtype, tag):
         assert np.all(err <= bound), f"{tag}: row {r} L={L} excess {float(np.max(err - bound)):.3g}"
 
 
-def run_case(B, M, S, D, dtype, lens, scale, seed):
+def run_case(B, M, S, D, dtype, lens, scale, seed, split="auto"):
     shape = (B, M, S, D)
     q, k, v = (workloads.scores_cpu(shape, dtype, 1.0, seed + i) for i in range(3))
     qs, ks, vs = (workloads.to_storage(t) for t in (q, k, v))
     ref = oracle.attention_f64(qs, ks, vs, lens, scale, dtype)
-    print(f"attention B={B} M={M} S={S} D={D} {DNAME[dtype]} lens={list(lens)}", flush=True)
+    print(f"attention B={B} M={M} S={S} D={D} {DNAME[dtype]} lens={list(lens)} split={split}",
+          flush=True)
     o = g.attention(q.cuda(), k.cuda(), v.cuda(), torch.as_tensor(np.asarray(lens, np.int32)).cuda(),
-                    scale)
+                    scale, split=split)
     torch.cuda.synchronize()
     o_st = workloads.to_storage(o.cpu())
     vf = to_f64(vs, dtype)
@@ -162,17 +163,19 @@ def test_attention_rejects_bad_arguments():
         g.attention(q, q.clone(), q.clone(), sl, out=q)
 
 
-@pytest.mark.parametrize("name", sorted(workloads.ATTN_WORKLOADS))
-def test_attention_full_workload(name):
-    """The benchmark's shapes at full size through the default entry point: every row of every
-    head against the oracle (one oracle call per head on host threads), padded rows +0 bit for
-    bit and kept rows within the bound."""
+@pytest.mark.parametrize("name,split", [(n, "auto") for n in sorted(workloads.ATTN_WORKLOADS)]
+                         + [("attn_f16_3x64x1000_d64", "on")])
+def test_attention_full_workload(name, split):
+    """The benchmark's shapes at full size through the default entry point (the automatic
+    work split takes whole tiles on both), and the small shape with the key split forced:
+    every row of every head against the oracle (one oracle call per head on host threads),
+    padded rows +0 bit for bit and kept rows within the bound."""
     w = workloads.ATTN_WORKLOADS[name]
     lens = workloads.seq_lens(w)
-    print(f"attention full workload {name} lens={list(lens)}", flush=True)
+    print(f"attention full workload {name} lens={list(lens)} split={split}", flush=True)
     q, k, v = (workloads.scores_device(w.shape, w.dtype, 1.0, w.x_seed + i, "cuda")
                for i in range(3))
-    o = g.attention(q, k, v, torch.as_tensor(lens).cuda(), w.scale)
+    o = g.attention(q, k, v, torch.as_tensor(lens).cuda(), w.scale, split=split)
     torch.cuda.synchronize()
     qs, ks, vs, os_ = (workloads.to_storage(t.cpu()) for t in (q, k, v, o))
     S, D = w.S, w.D
@@ -232,4 +235,98 @@ def test_attention_plane_major_head_size_128():
     with ThreadPoolExecutor(max_workers=host_threads()) as pool:
         worst = max(pool.map(one, [(b, m) for b in range(B) for m in range(M)]))
     print(f"plane-major D=128: every row of every head checked, worst error {worst:.3g}",
+          flush=True)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DNAME[d])
+@pytest.mark.parametrize("split", ["off", "on"])
+def test_attention_key_split(dtype, split):
+    """Head size 64 with each work split forced: whole tiles per workgroup, or each tile's key
+    blocks split between two groups of wavefronts and merged (flash_decoding.py's split-KV
+    reduction). Lengths give tiles of one key block (the first group then has none), two,
+    and odd counts (the second group has one more), rows past the length, a length past S;
+    the scales include 0 and a negative one; rising scores move the running max in one group
+    and not the other. At head size 128 the choice is ignored: same bits."""
+    for S in (1, 33, 64, 65, 127, 128, 129, 200, 300, 1000):
+        lens = [S, max(1, S // 3), 0, S + 7]
+        run_case(len(lens), 2, S, 64, dtype, lens, 0.125, seed=20 * S + 3, split=split)
+    for scale in (0.0, -0.125, 2.0):
+        run_case(2, 2, 300, 64, dtype, [300, 97], scale, seed=801, split=split)
+    S, lens, scale = 640, [640, 300], 0.125
+    shape = (2, 1, S, 64)
+    q, k, v = (workloads.scores_cpu(shape, workloads.F32, 1.0, 95 + i) for i in range(3))
+    q.mul_(0.05)
+    k.mul_(0.05)
+    q[..., 0] = 1.0
+    k[..., 0] = torch.arange(S, dtype=torch.float32) * (16.0 / 64.0 / (scale * np.log2(np.e)))
+    q, k, v = (t.to(workloads.torch_dtype(dtype)) for t in (q, k, v))
+    qs, ks, vs = (workloads.to_storage(t) for t in (q, k, v))
+    ref = oracle.attention_f64(qs, ks, vs, lens, scale, dtype)
+    o = g.attention(q.cuda(), k.cuda(), v.cuda(), torch.as_tensor(np.asarray(lens, np.int32)).cuda(),
+                    scale, split=split)
+    torch.cuda.synchronize()
+    o_st = workloads.to_storage(o.cpu())
+    vf = to_f64(vs, dtype)
+    for b in range(2):
+        check_rows(o_st[b, 0], ref[b, 0], prefix_vmax(vf[b, 0]), [lens[b]] * S, range(S), S,
+                   dtype, f"rising split={split} {DNAME[dtype]} b={b}")
+    q, k, v = (workloads.scores_device((2, 2, 300, 128), dtype, 1.0, 900 + i, "cuda")
+               for i in range(3))
+    sl = torch.as_tensor(np.asarray([300, 111], np.int32)).cuda()
+    a, b = g.attention(q, k, v, sl, split=split), g.attention(q, k, v, sl, split="auto")
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_attention_key_split_ignores_padding():
+    """With the key split, queries of padded rows and keys/values at or past the length still
+    change no bit."""
+    B, M, S, D = 3, 2, 260, 64
+    lens = [260, 97, 0]
+    sl = torch.as_tensor(np.asarray(lens, np.int32)).cuda()
+    q, k, v = (workloads.scores_device((B, M, S, D), workloads.BF16, 1.0, 950 + i, "cuda")
+               for i in range(3))
+    clean = g.attention(q, k, v, sl, split="on")
+    qp, kp, vp = q.clone(), k.clone(), v.clone()
+    for b, L in enumerate(lens):
+        for t in (qp, kp, vp):
+            t[b, :, L:] = float("nan")
+    dirty = g.attention(qp, kp, vp, sl, split="on")
+    torch.cuda.synchronize()
+    assert torch.equal(clean.view(torch.int16), dirty.view(torch.int16))
+
+
+def test_attention_auto_split_small_grid():
+    """bf16 [2, 8, 4096, 64]: 512 (head, tile) pairs, where the automatic choice takes the key
+    split (same bits as forcing it). Every row of every head against the oracle (one oracle
+    call per head on host threads)."""
+    B, M, S, D = 2, 8, 4096, 64
+    lens = np.asarray([4096, 3001], np.int32)
+    q, k, v = (workloads.scores_device((B, M, S, D), workloads.BF16, 1.0, 3200 + i, "cuda")
+               for i in range(3))
+    sl = torch.as_tensor(lens).cuda()
+    o = g.attention(q, k, v, sl, 0.125)
+    forced = g.attention(q, k, v, sl, 0.125, split="on")
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), forced.view(torch.int16))
+    qs, ks, vs, os_ = (workloads.to_storage(t.cpu()) for t in (q, k, v, o))
+
+    def one(bm):
+        b, m = bm
+        L = int(lens[b])
+        assert not bits(os_[b, m])[L:].any(), f"b={b} m={m}: padded rows are not zero"
+        ref = oracle.attention_f64(qs[b:b + 1, m:m + 1], ks[b:b + 1, m:m + 1],
+                                   vs[b:b + 1, m:m + 1], lens[b:b + 1], 0.125,
+                                   workloads.BF16)[0, 0, :L]
+        got = to_f64(os_[b, m, :L], workloads.BF16)
+        vmax = prefix_vmax(to_f64(vs[b, m], workloads.BF16))[:L, None]
+        err = np.abs(got - ref)
+        bound = U[workloads.BF16] * (vmax + np.abs(ref)) + 1e-5 * vmax
+        assert np.all(np.isfinite(got)), f"b={b} m={m}: non-finite output"
+        assert np.all(err <= bound), f"b={b} m={m}: excess {float(np.max(err - bound)):.3g}"
+        return float(err.max())
+
+    with ThreadPoolExecutor(max_workers=host_threads()) as pool:
+        worst = max(pool.map(one, [(b, m) for b in range(B) for m in range(M)]))
+    print(f"bf16 [2, 8, 4096, 64] key split: every row checked, worst error {worst:.3g}",
           flush=True)

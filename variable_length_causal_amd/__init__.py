@@ -66,6 +66,8 @@ def _load():
     lib.gtms_backward_masked.restype = i32
     lib.gtms_attention_forward.argtypes = [p, p, p, p, p, i64, i64, i64, i64, f32, i32, p]
     lib.gtms_attention_forward.restype = i32
+    lib.gtms_attention_forward_ex.argtypes = [p, p, p, p, p, i64, i64, i64, i64, f32, i32, i32, p]
+    lib.gtms_attention_forward_ex.restype = i32
     lib.gtms_status_string.argtypes = [i32]
     lib.gtms_status_string.restype = ctypes.c_char_p
     lib.gtms_version.argtypes = []
@@ -328,11 +330,15 @@ def backward_masked(y, dy, mask, seq_lens=None, scale: float = 1.0, out=None,
     return out
 
 
-def attention(q, k, v, seq_lens, scale: float | None = None, out=None):
+ATTN_SPLITS = {"auto": 0, "off": 1, "on": 2}
+
+
+def attention(q, k, v, seq_lens, scale: float | None = None, out=None, split: str = "auto"):
     """Fused attention with the grouped tril mask: for query row r < L_b,
     out[r] = sum_{c <= r} softmax_c(scale * q[r].k[c]) v[c]; rows r >= L_b are zero.
     q, k, v: [B, M, S, D] float16 or bfloat16 GPU tensors, D = 64 or 128. The default scale
-    is 1 / sqrt(D)."""
+    is 1 / sqrt(D). split: "auto", "off" or "on", the key split of each query tile over two
+    groups of wavefronts (head size 64; see gtms_attention_forward_ex)."""
     import math
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -350,8 +356,8 @@ def attention(q, k, v, seq_lens, scale: float | None = None, out=None):
     sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
     L = _load()
     with _on_device(q):
-        st = L.gtms_attention_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                      seq_lens.data_ptr(), B, M, S, D, sc, _dtype_code(q),
-                                      _stream_of(q))
-    _raise(st, "gtms_attention_forward")
+        st = L.gtms_attention_forward_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                         out.data_ptr(), seq_lens.data_ptr(), B, M, S, D, sc,
+                                         _dtype_code(q), ATTN_SPLITS[split], _stream_of(q))
+    _raise(st, "gtms_attention_forward_ex")
     return out

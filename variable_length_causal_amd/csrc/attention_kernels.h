@@ -75,8 +75,15 @@ __device__ __forceinline__ float swap_halves(float v) {
         (int)((threadIdx.x ^ 32) & 63) * 4, __builtin_bit_cast(int, v)));
 }
 
-template <int DT, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : 2))) void attn_fwd(AttnArgs a) {
+// SPLIT = 2 (head size 64): the workgroup has two groups of 4 wavefronts on the same 128 query
+// rows; group 0 takes the tile's first floor(n/2) key blocks, group 1 the rest (the diagonal
+// blocks included). Each group keeps its own online (max, sum) and accumulators over its keys,
+// and group 0 merges group 1's partials through LDS at the end by the split-KV reduction of
+// flash_decoding.py (_flash_decoding_fwd_reduce_kernel): m = max(m0, m1), l = sum_i l_i 2^(m_i - m),
+// O = sum_i O_i 2^(m_i - m). A tile's chain of key blocks, which sets the launch's length when
+// there are few tiles per CU, is then half as long.
+template <int DT, int D, int SPLIT>
+__global__ __launch_bounds__(256 * SPLIT) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : 2))) void attn_fwd(AttnArgs a) {
     using MF = Mfma16<DT>;
     using vec8 = typename MF::vec8;
     using elem_t = typename MF::elem_t;
@@ -90,10 +97,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3
     constexpr int KCH = BN * CPR / 256;    // K chunks per thread per block
     constexpr int VCH = BN / 2 * CPR / 256;  // V key pairs (two chunks) per thread per block
     static_assert(KCH >= 1 && VCH >= 1 && BN % 32 == 0, "block shape");
+    static_assert(SPLIT == 1 || (SPLIT == 2 && D == 64), "key split at head size 64 only");
     // two buffers: block i computes from buffer i % 2 while block i + 1 is written into the
     // other one
-    __shared__ __attribute__((aligned(16))) elem_t k_lds[2][BN * KP];
-    __shared__ __attribute__((aligned(16))) elem_t vt_lds[2][D * VP];
+    __shared__ __attribute__((aligned(16))) elem_t k_lds_all[SPLIT][2][BN * KP];
+    __shared__ __attribute__((aligned(16))) elem_t vt_lds_all[SPLIT][2][D * VP];
 
     // Block order, chosen by the host:
     //  - tile-major: the last tile of every plane first, then the one before, and so on, so
@@ -117,7 +125,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3
     }
     const int q0 = qt * kAttnRows;
     const int L = clamp_len(a.seq_lens[plane / a.M], a.S);
-    const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6), g = lane >> 5;
+    // grp: the key group (0 unless SPLIT = 2); tid: the thread within its group
+    const int grp = SPLIT == 1 ? 0 : uniform((int)threadIdx.x >> 8);
+    const int tid = threadIdx.x & 255, lane = tid & 63, wave = uniform(tid >> 6), g = lane >> 5;
+    auto& k_lds = k_lds_all[grp];
+    auto& vt_lds = vt_lds_all[grp];
     const uint64_t head = (uint64_t)plane * (uint64_t)a.S * D;  // first element of the head
     const uint32_t head_bytes = (uint32_t)((uint64_t)a.S * D * 2);
     const rsrc_t out = make_rsrc((const char*)a.o + head * 2, head_bytes);
@@ -125,7 +137,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3
     // rows q0 .. q0+127 that lie at or past L are zeros (all of them when q0 >= L)
     {
         const int z0 = max(q0, L), z1 = min(q0 + kAttnRows, a.S);
-        for (int i = tid; i < (z1 - z0) * CPR; i += 256) {
+        for (int i = (int)threadIdx.x; i < (z1 - z0) * CPR; i += 256 * SPLIT) {
             const int r = z0 + i / CPR, c = (i % CPR) * 8;
             __builtin_amdgcn_raw_buffer_store_b128(u32x4{0, 0, 0, 0}, out, (r * D + c) * 2, 0,
                                                    kPolicyNt);
@@ -204,13 +216,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3
     for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
     float m_run = -INFINITY, l_part = 0.0f;
 
+    // The group's key blocks [k_begin, k_end): all of [0, kv_end) unless SPLIT = 2, where
+    // group 0 takes the first nb0 = floor(nb / 2) blocks and group 1 the others.
+    const int nb = (kv_end + BN - 1) / BN, nb0 = SPLIT == 1 ? 0 : nb / 2;
+    const int k_begin = grp == 0 ? 0 : nb0 * BN;
+    const int k_end = SPLIT == 2 && grp == 0 ? nb0 * BN : kv_end;
+
     // Pipeline: global loads run two blocks ahead of the computation, LDS writes one block
     // ahead; one barrier per block separates the writes of a buffer from its readers.
-    fetch(0);
-    stage(0);
-    if (BN < kv_end) fetch(BN);
+    if (k_begin < k_end) {
+        fetch(k_begin);
+        stage(0);
+        if (k_begin + BN < k_end) fetch(k_begin + BN);
+    }
     __syncthreads();
-    for (int kb = 0, buf = 0; kb < kv_end; kb += BN, buf ^= 1) {
+    for (int kb = k_begin, buf = 0; kb < k_end; kb += BN, buf ^= 1) {
         {  // a wavefront whose rows need no key of the block computes it masked
 
         // S^T[key][row] for the 32-key tiles of the block that this wavefront needs
@@ -297,11 +317,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3
         }  // kb < wave_end
         // the next block into the other buffer (its readers finished before the last
         // barrier), then the loads of the block after it
-        if (kb + BN < kv_end) {
+        if (kb + BN < k_end) {
             stage(buf ^ 1);
-            if (kb + 2 * BN < kv_end) fetch(kb + 2 * BN);
+            if (kb + 2 * BN < k_end) fetch(kb + 2 * BN);
         }
         __syncthreads();
+    }
+    if constexpr (SPLIT == 2) {
+        // Group 0 has nb0 blocks, group 1 nb - nb0 (at most one more): the barrier count of
+        // group 0 is made up here (a barrier waits for every wavefront's arrival, wherever
+        // in the code it is).
+        if (grp == 0 && nb - nb0 > nb0) __syncthreads();
+        // Group 1's partials go through the K buffers (free since the last barrier: their
+        // last reads came before it), 34 floats per lane laid out [wave][value][lane].
+        float* part = reinterpret_cast<float*>(&k_lds_all[0][0][0]) + wave * 34 * 64 + lane;
+        static_assert(4 * 34 * 64 * 4 <= sizeof(k_lds_all), "merge area");
+        if (grp == 1) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) part[(16 * t + e) * 64] = acc[t][e];
+            }
+            part[32 * 64] = m_run;
+            part[33 * 64] = l_part;
+        }
+        __syncthreads();
+        if (grp == 1) return;
+        // m_run is a row's reference in the log2 domain (equal on both lanes of the row, in
+        // each group); the partials are sums relative to 2^m_run
+        const float m1 = part[32 * 64], l1 = part[33 * 64];
+        const float m = fmaxf(m_run, m1);
+        const float a0 = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m);
+        const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
+        l_part = l_part * a0 + l1 * a1;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[t][e] = acc[t][e] * a0 + part[(16 * t + e) * 64] * a1;
+        }
     }
 
     // Normalise and store the rows below L (acc[t] register e: d = 32t + 8*(e/4) + 4g + e%4).

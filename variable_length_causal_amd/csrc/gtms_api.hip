@@ -222,8 +222,9 @@ int run_impl(const void* x, const void* g, void* out, const int32_t* seq_lens, i
 
 int attention_impl(const void* q, const void* k, const void* v, void* out,
                    const int32_t* seq_lens, int64_t B, int64_t M, int64_t S, int64_t D,
-                   float scale, int dtype, void* stream) {
+                   float scale, int dtype, int split, void* stream) {
     if (dtype != GTMS_F16 && dtype != GTMS_BF16) return GTMS_ERR_DTYPE;
+    if (split < GTMS_ATTN_SPLIT_AUTO || split > GTMS_ATTN_SPLIT_ON) return GTMS_ERR_PATH;
     if (B < 0 || M < 0 || S < 0 || D < 0 || S > GTMS_MAX_S || M > INT32_MAX)
         return GTMS_ERR_INVALID_ARG;
     int64_t planes = 0, bytes = 0;
@@ -256,7 +257,7 @@ int attention_impl(const void* q, const void* k, const void* v, void* out,
     a.S = (int)S;
     a.n_tiles = (int)tiles;
     a.k2 = (float)((double)scale * 1.4426950408889634074);
-    const hipError_t e = launch_attention(dtype, (int)D, a, (hipStream_t)stream);
+    const hipError_t e = launch_attention(dtype, (int)D, a, split, (hipStream_t)stream);
     return e == hipSuccess ? GTMS_OK : GTMS_ERR_HIP;
 }
 
@@ -359,7 +360,14 @@ int gtms_backward_masked(const void* y, const void* dy, void* dx, const uint8_t*
 int gtms_attention_forward(const void* q, const void* k, const void* v, void* out,
                            const int32_t* seq_lens, int64_t B, int64_t M, int64_t S, int64_t D,
                            float scale, int dtype, void* stream) {
-    return gtms::attention_impl(q, k, v, out, seq_lens, B, M, S, D, scale, dtype, stream);
+    return gtms::attention_impl(q, k, v, out, seq_lens, B, M, S, D, scale, dtype,
+                                GTMS_ATTN_SPLIT_AUTO, stream);
+}
+
+int gtms_attention_forward_ex(const void* q, const void* k, const void* v, void* out,
+                              const int32_t* seq_lens, int64_t B, int64_t M, int64_t S,
+                              int64_t D, float scale, int dtype, int split, void* stream) {
+    return gtms::attention_impl(q, k, v, out, seq_lens, B, M, S, D, scale, dtype, split, stream);
 }
 
 const char* gtms_status_string(int status) {
@@ -374,6 +382,6 @@ const char* gtms_status_string(int status) {
     }
 }
 
-int gtms_version(void) { return 200; }
+int gtms_version(void) { return 300; }
 
 }  // extern "C"

@@ -57,8 +57,18 @@ extern template hipError_t launch_kind<OP_BWD, MK_TRIL>(int, const Plan&, const 
 extern template hipError_t launch_kind<OP_BWD, MK_BAND>(int, const Plan&, const FwdArgs&, hipStream_t);
 extern template hipError_t launch_kind<OP_BWD, MK_MASK>(int, const Plan&, const FwdArgs&, hipStream_t);
 
+// The automatic choice of the attention's key split (head size 64): grids of at most
+// kAttnSplitBlocksPerCU (plane, query tile) blocks per compute unit, all of them resident at
+// once on the whole-tile kernel (three workgroups per CU), with rows of at least
+// kAttnSplitMinS. There the longest tile's chain of key blocks sets the launch's length, and
+// halving it gained 14-31% on MI355X over ten such shapes (bf16 and f16 [1-3, 4-16, 2048-16384,
+// 64]); with more blocks than resident slots, or shorter rows, the split lost 3-31% (one
+// workgroup per CU instead of three) or gained nothing.
+constexpr int64_t kAttnSplitBlocksPerCU = 3;
+constexpr int kAttnSplitMinS = 2048;
+
 // Launches the fused attention kernel for element type `dtype` (GTMS_F16 or GTMS_BF16) and
-// head size D (64 or 128).
-hipError_t launch_attention(int dtype, int D, const AttnArgs& a, hipStream_t st);
+// head size D (64 or 128); split is a GTMS_ATTN_SPLIT_* choice.
+hipError_t launch_attention(int dtype, int D, const AttnArgs& a, int split, hipStream_t st);
 
 }  // namespace gtms

@@ -5,8 +5,26 @@
 #include "launch.h"
 
 namespace gtms {
+namespace {
 
-hipError_t launch_attention(int dtype, int D, const AttnArgs& args, hipStream_t st) {
+// Compute units of the current device (256 on MI355X), queried once per device.
+int64_t compute_units() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+}  // namespace
+
+hipError_t launch_attention(int dtype, int D, const AttnArgs& args, int split, hipStream_t st) {
     AttnArgs a = args;
     // Block order (measured on MI355X over 10 shapes, D = 64 and 128): tile-major (longest
     // tiles of all planes first) gained 2-32% whenever the heads' K and V together fit in
@@ -16,13 +34,19 @@ hipError_t launch_attention(int dtype, int D, const AttnArgs& args, hipStream_t 
     // one XCD's L2.
     const int64_t kv_bytes = int64_t(2) * a.n_planes * a.S * D * 2;
     a.tile_major = kv_bytes <= (int64_t(192) << 20) || a.S <= 2048;
-    const dim3 grid((unsigned)((uint64_t)a.n_planes * (uint64_t)a.n_tiles)), block(256);
+    const int64_t blocks = (int64_t)a.n_planes * a.n_tiles;
+    const bool two = D == 64 && (split == GTMS_ATTN_SPLIT_ON ||
+                                 (split == GTMS_ATTN_SPLIT_AUTO && a.S >= kAttnSplitMinS &&
+                                  blocks <= kAttnSplitBlocksPerCU * compute_units()));
+    const dim3 grid((unsigned)blocks), block(two ? 512 : 256);
     if (dtype == GTMS_BF16) {
-        if (D == 64) hipLaunchKernelGGL((attn_fwd<DT_BF16, 64>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((attn_fwd<DT_BF16, 128>), grid, block, 0, st, a);
+        if (D == 128) hipLaunchKernelGGL((attn_fwd<DT_BF16, 128, 1>), grid, block, 0, st, a);
+        else if (two) hipLaunchKernelGGL((attn_fwd<DT_BF16, 64, 2>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((attn_fwd<DT_BF16, 64, 1>), grid, block, 0, st, a);
     } else {
-        if (D == 64) hipLaunchKernelGGL((attn_fwd<DT_F16, 64>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((attn_fwd<DT_F16, 128>), grid, block, 0, st, a);
+        if (D == 128) hipLaunchKernelGGL((attn_fwd<DT_F16, 128, 1>), grid, block, 0, st, a);
+        else if (two) hipLaunchKernelGGL((attn_fwd<DT_F16, 64, 2>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((attn_fwd<DT_F16, 64, 1>), grid, block, 0, st, a);
     }
     return hipGetLastError();
 }
