@@ -185,7 +185,8 @@ def bench_attention(args):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": MFMA16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(f"{w.name}:attention")},
+                     "traffic": measured_traffic(
+                         f"{w.name}:attention" + ("" if args.split == "auto" else f":split-{args.split}"))},
         "cpu_baseline": None,
         "device": device_info(),
     }
@@ -292,7 +293,7 @@ def measured_traffic(key: str):
     except (OSError, ValueError):
         return None
     ent = data.get(key)
-    family = "attention" if key.endswith(":attention") else "softmax"
+    family = "attention" if ":attention" in key else "softmax"
     if not ent or ent.get("kernel_sources_sha256") != kernel_sources_hash(family):
         return None
     return ent.get("hbm_bytes_per_launch")

@@ -167,9 +167,10 @@ def test_attention_rejects_bad_arguments():
                          + [("attn_f16_3x64x1000_d64", "on")])
 def test_attention_full_workload(name, split):
     """The benchmark's shapes at full size through the default entry point (the automatic
-    work split takes whole tiles on both), and the small shape with the key split forced:
-    every row of every head against the oracle (one oracle call per head on host threads),
-    padded rows +0 bit for bit and kept rows within the bound."""
+    work split takes whole tiles on the two larger grids and the key split on bf16
+    2 x 8 x 4096), and f16 3 x 64 x 1000 with the key split forced: every row of every head
+    against the oracle (one oracle call per head on host threads), padded rows +0 bit for bit
+    and kept rows within the bound."""
     w = workloads.ATTN_WORKLOADS[name]
     lens = workloads.seq_lens(w)
     print(f"attention full workload {name} lens={list(lens)} split={split}", flush=True)

@@ -112,6 +112,11 @@ ATTN_WORKLOADS = {
     # readme_f32_3x64x1000
     "attn_f16_3x64x1000_d64": AttnWorkload("attn_f16_3x64x1000_d64", 3, 64, 1000, 64, F16,
                                            1, 1000, x_seed=1102, len_seed=2002),
+    # two sequences of the batch-32 shape above (a small batch of long rows): 512 (head, query
+    # tile) pairs, two per compute unit, where each tile's keys are split over two groups of
+    # wavefronts (flash_decoding.py's split-KV reduction)
+    "attn_bf16_2x8x4096_d64": AttnWorkload("attn_bf16_2x8x4096_d64", 2, 8, 4096, 64, BF16,
+                                           fixed_lens=(4096, 3001), x_seed=1105, len_seed=2005),
 }
 
 
