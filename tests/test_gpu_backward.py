@@ -287,7 +287,8 @@ def test_backward_stash_rows():
     [0, 2/n) over the kept set (n its width) and zero elsewhere, dy normal. With y zero
     outside the window, D and every kept dx of the window equal those of the grouped tril
     mask, so every element compares with the oracle's tril backward rows; the window's
-    masked elements must also be +0 bit for bit."""
+    masked elements must also be +0 bit for bit. Paired rows and dx written over dy give the
+    same bits."""
     cases = ((workloads.F32, 40000, 40000 - 3, None, 0.7),
              (workloads.BF16, 100000, 100000 - 5, -70000, 0.3))
     for dtype, S, L, lo, scale in cases:
@@ -307,9 +308,22 @@ def test_backward_stash_rows():
         lens = np.asarray([L], np.int32)
         worst = check_rows_backward_against_oracle(y, dy, dx, lens, scale, dtype, U[dtype],
                                                    TINY[dtype])
+        ib = torch.int32 if dtype == workloads.F32 else torch.int16
         if lo is not None:
-            ib = torch.int32 if dtype == workloads.F32 else torch.int16
             assert torch.equal(dx.triu(lo).view(ib), dx.view(ib)), "window: masked bits set"
+        # the same bits with rows r and S-1-r paired in one unit (two rows through one stash
+        # in turn), and with dx written over dy (both passes read dy before any dx store)
+        paired = (g.backward(y, dy, sl, scale, flags=1) if lo is None
+                  else g.backward_band(y, dy, sl, lo, 0, scale, flags=1))
+        inplace = dy.clone()
+        if lo is None:
+            g.backward(y, inplace, sl, scale, out=inplace)
+        else:
+            g.backward_band(y, inplace, sl, lo, 0, scale, out=inplace)
+        torch.cuda.synchronize()
+        assert torch.equal(paired.view(ib), dx.view(ib)), "paired rows changed bits"
+        assert torch.equal(inplace.view(ib), dx.view(ib)), "in place changed bits"
+        del paired, inplace
         print(f"S={S}: every element checked, worst error {worst:.3g}", flush=True)
         del y, dy, dx
         torch.cuda.empty_cache()
