@@ -5,14 +5,21 @@
 // section 2.1) and z = scale * x give
 //   dx_c = scale * y_c * (g_c - D),   D = sum over kept k of g_k * y_k,
 // for kept c; every other element of dx is +0 (masked elements and padded rows do not
-// reach the output). The kept set follows the mask kind MK of the forward kernels. Arithmetic is fp32; results are rounded to nearest-even into the
-// element type.
+// reach the output). The kept set follows the mask kind MK of the forward kernels.
+// Arithmetic is fp32; results are rounded to nearest-even into the element type.
 //
 // Memory: reads the kept intervals of y and g (for the tril mask, two triangles), with
 // non-temporal loads where the read is the last; writes every row of dx in full. The layout,
 // buffer-resource range checks, non-temporal stores, live-slot specialisation and line
 // ownership are those of the forward kernels; the reduction is a plain sum (wave DPP +
 // readlane, then LDS across the waves of a workgroup).
+//
+// Four kernels:
+//   bwd_wave   one wavefront per row, y and g held in registers;
+//   bwd_block  one workgroup of W wavefronts per row, up to 8 vectors of each per lane;
+//   bwd_stash  16 wavefronts per row, 8 vectors per lane in registers and the rest of the
+//              row (up to kStashVecs pairs) in LDS, for the computed masks on 16-byte rows;
+//   bwd_stream one workgroup per row, two passes over both intervals, any length.
 #pragma once
 
 #include "forward_kernels.h"
