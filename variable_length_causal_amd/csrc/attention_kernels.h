@@ -148,7 +148,6 @@ __global__ __launch_bounds__(256 * SPLIT) __attribute__((amdgpu_waves_per_eu(D <
     const int row = q0 + wave * 32 + (lane & 31);      // this lane's query row
     const int row_lo = q0 + wave * 32;                 // the wavefront's first row
     const int kv_end = min(q0 + kAttnRows, L);         // keys the workgroup needs
-    const int wave_end = min(row_lo + 32, L);          // keys this wavefront needs
 
     // Q^T as the B operand: lane l holds Q[row][16*kk + 8*g + j]
     const rsrc_t qin = make_rsrc((const char*)a.q + head * 2, head_bytes);
@@ -314,7 +313,7 @@ __global__ __launch_bounds__(256 * SPLIT) __attribute__((amdgpu_waves_per_eu(D <
                 }
             }
         }
-        }  // kb < wave_end
+        }
         // the next block into the other buffer (its readers finished before the last
         // barrier), then the loads of the block after it
         if (kb + BN < k_end) {
