@@ -179,6 +179,7 @@ def bench_attention(args):
         "config": {"workload": w.name, "op": "attention", "split": args.split,
                    "B": w.B, "M": w.M, "S": w.S,
                    "D": w.D, "seq_lens": [int(v) for v in lens], "scale": w.scale,
+                   "x_seed": w.x_seed, "len_seed": None if w.fixed_lens else w.len_seed,
                    "flops_per_step": flops,
                    "kernel_ms_min": round(float(np.min(kernel_ms)), 5),
                    "kernel_ms_median": round(float(np.median(kernel_ms)), 5)},
@@ -191,14 +192,16 @@ def bench_attention(args):
         "device": device_info(),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_attention(qkv[0], lens, w, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline_attention(qkv[0], outs[0], lens, w, args.cpu_budget)
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline_attention(qkv_dev, lens, w: workloads.AttnWorkload, budget_s: float):
+def cpu_baseline_attention(qkv_dev, o_dev, lens, w: workloads.AttnWorkload, budget_s: float):
     """Time the CPU oracle's attention, as it stands, on whole heads of the same input: one
     oracle call per head on T host threads, over the first k heads of every batch, k as many
-    as fit the time budget (wall seconds)."""
+    as fit the time budget (wall seconds). After the timing, the oracle's fp64 output of
+    those heads is compared with the GPU's output o_dev of the same input: the largest
+    absolute difference is reported."""
     from concurrent.futures import ThreadPoolExecutor
 
     import oracle
@@ -212,15 +215,21 @@ def cpu_baseline_attention(qkv_dev, lens, w: workloads.AttnWorkload, budget_s: f
     qs, ks, vs = (workloads.to_storage(t[:, :k].contiguous().cpu()) for t in qkv_dev)
     tasks = [(b, m) for b in range(w.B) for m in range(k)]
 
+    outs = {}
+
     def run(task):
         b, m = task
-        oracle.attention_f64(qs[b:b + 1, m:m + 1], ks[b:b + 1, m:m + 1], vs[b:b + 1, m:m + 1],
-                             lens[b:b + 1], w.scale, w.dtype)
+        outs[task] = oracle.attention_f64(qs[b:b + 1, m:m + 1], ks[b:b + 1, m:m + 1],
+                                          vs[b:b + 1, m:m + 1], lens[b:b + 1], w.scale, w.dtype)
 
     with ThreadPoolExecutor(max_workers=T) as pool:
         t0 = time.perf_counter()
         list(pool.map(run, tasks))
         dt = time.perf_counter() - t0
+    diff = 0.0
+    for (b, m), ref in outs.items():
+        got = o_dev[b, m].double().cpu().numpy()
+        diff = max(diff, float(np.max(np.abs(got - ref[0, 0]))))
     sub = workloads.AttnWorkload(w.name, w.B, k, w.S, w.D, w.dtype, w.len_lo, w.len_hi)
     flops = attention_flops(sub, lens)
     what = "all heads" if k == w.M else f"heads m < {k} of every batch"
@@ -233,6 +242,7 @@ def cpu_baseline_attention(qkv_dev, lens, w: workloads.AttnWorkload, budget_s: f
                   f"same seeded input, fp64 C oracle (single-threaded), one call per head on "
                   f"{T} host threads, {dt:.2f} s wall",
         "cpu": cpu_model(),
+        "max_abs_diff_vs_gpu": diff,
     }
 
 
@@ -309,12 +319,14 @@ def host_threads() -> int:
     return int(max(1, min(16, n)))
 
 
-def cpu_baseline(x_dev, lens, w: workloads.Workload, budget_s: float,
+def cpu_baseline(x_dev, y_dev, lens, w: workloads.Workload, budget_s: float,
                  max_host_bytes: int = 4 << 30):
     """Time the CPU oracle, as it stands, on whole planes of the same input: all planes if
     they fit the time budget (wall seconds) and the host-memory cap, else planes m < k of
     every batch. The oracle is single-threaded; independent planes run concurrently, one
-    oracle call per plane, on T host threads (ctypes releases the GIL during each call)."""
+    oracle call per plane, on T host threads (ctypes releases the GIL during each call).
+    After the timing, the oracle's (rounded) output of those planes is compared with the
+    GPU's output y_dev of the same input: the largest absolute difference is reported."""
     from concurrent.futures import ThreadPoolExecutor
 
     import oracle
@@ -333,14 +345,21 @@ def cpu_baseline(x_dev, lens, w: workloads.Workload, budget_s: float,
     torch.cuda.synchronize()
     tasks = [(b, m) for b in range(w.B) for m in range(k)]
 
+    outs = {}
+
     def run(task):
         b, m = task
-        oracle.softmax(sample[b:b + 1, m:m + 1], lens[b:b + 1], w.scale, w.dtype)
+        outs[task] = oracle.softmax(sample[b:b + 1, m:m + 1], lens[b:b + 1], w.scale, w.dtype)
 
     with ThreadPoolExecutor(max_workers=T) as pool:
         t0 = time.perf_counter()
         list(pool.map(run, tasks))
         dt = time.perf_counter() - t0
+    diff = 0.0
+    for (b, m), ref in outs.items():
+        got = y_dev[b, m].double().cpu()
+        want = workloads.from_storage(ref[0, 0], w.dtype).double()
+        diff = max(diff, float((got - want).abs().max()))
     sub = workloads.Workload(w.name, w.B, k, w.S, w.dtype, w.sigma, w.scale)
     nbytes = algorithmic_bytes(sub, lens)
     what = "all planes" if k == w.M else f"planes m < {k} of every batch"
@@ -353,6 +372,7 @@ def cpu_baseline(x_dev, lens, w: workloads.Workload, budget_s: float,
                   f"algorithmic) of the same seeded input, fp64 C oracle (single-threaded), "
                   f"one call per plane on {T} host threads, {dt:.2f} s wall",
         "cpu": cpu_model(),
+        "max_abs_diff_vs_gpu": diff,
     }
 
 
@@ -522,6 +542,8 @@ def main():
             "B": w.B, "M": w.M, "S": w.S,
             "seq_lens": [int(v) for v in lens],
             "scale": w.scale,
+            "x_seed": w.x_seed,
+            "len_seed": None if w.fixed_lens else w.len_seed,
             "path": args.path,
             "bytes_per_step": step_bytes,
             "kernel_ms_min": round(float(np.min(kernel_ms)), 5),
@@ -543,7 +565,9 @@ def main():
     # take minutes and tens of GB of host memory, so their lines carry no baseline
     if not args.no_cpu_baseline and args.op == "forward" and args.variant == "tril" \
             and w.S * w.S <= (1 << 26):
-        out["cpu_baseline"] = cpu_baseline(xs[0], lens, w, args.cpu_budget)
+        step(0)  # the context kernels above overwrote ys: the forward of xs[0] again
+        torch.cuda.synchronize()
+        out["cpu_baseline"] = cpu_baseline(xs[0], ys[0], lens, w, args.cpu_budget)
     print(json.dumps(out), flush=True)
 
 
