@@ -532,7 +532,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": workloads.DTYPE_NAMES[w.dtype],
+        # the arithmetic the kernels compute in: fp32 for every element type (the element
+        # type of the tensors is config.io_dtype)
+        "dtype": "f32",
         "data": "synthetic (seeded normal scores generated on the device, seeded lengths)",
         "config": {
             "workload": w.name,
@@ -540,6 +542,7 @@ def main():
             "variant": args.variant if args.variant == "tril" else
             (f"band lo={lo} hi={hi}" if args.variant == "band" else f"mask tril({hi}) [1,1,S,S]"),
             "B": w.B, "M": w.M, "S": w.S,
+            "io_dtype": workloads.DTYPE_NAMES[w.dtype],
             "seq_lens": [int(v) for v in lens],
             "scale": w.scale,
             "x_seed": w.x_seed,
