@@ -140,3 +140,22 @@ def test_oracle_forward_to_device(dtype):
         from gtms_check import bits, to_f64
         assert not bits(got_r)[ref == 0].any()
         assert np.max(np.abs(to_f64(got_r, dtype) - ref)) <= 2.0 ** -8 * max(1.0, np.max(ref))
+
+
+@pytest.mark.parametrize("dtype", [workloads.F32, workloads.F16, workloads.BF16])
+def test_window_by_minus_infinity(dtype):
+    """The reduction behind the long-row band tests: with the scores below a causal window set
+    to -inf, the oracle's grouped tril softmax (whole tensor and row entry point) equals its
+    band softmax of the same input exactly, masked cells +0 included."""
+    S, lo, L = 12, -4, 10
+    x = workloads.scores_cpu((1, 1, S, S), dtype, 1.0, seed=61)
+    for r in range(S):
+        for c in range(S):
+            if c < r + lo:
+                x[0, 0, r, c] = float("-inf")
+    xs = workloads.to_storage(x)
+    band = oracle.softmax_band_f64(xs, [L], lo, 0, 0.3, dtype)
+    tril = oracle.softmax_f64(xs, [L], 0.3, dtype)
+    rows = oracle.softmax_rows_f64(xs[0, 0], np.arange(S), [L] * S, 0.3, dtype)
+    assert np.array_equal(tril.view(np.uint64), band.view(np.uint64))
+    assert np.array_equal(rows.view(np.uint64), band[0, 0].view(np.uint64))

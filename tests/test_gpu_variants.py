@@ -404,3 +404,27 @@ def test_full_size_window_and_key_mask_backwards():
                                                  TINY[w.dtype], plane_ref=ref_key)
     print(f"key mask backward on {w.name}: every plane checked, worst error {worst:.3g}",
           flush=True)
+
+
+def test_band_forward_raw_long_rows():
+    """A causal window of 70001 columns on bfloat16 rows of 100000 (forward): each row holds only
+    its interval, up to 8766 vectors, which takes the block path at 16 raw vectors per lane.
+    The scores below the window are set to -inf, so the grouped tril mask's softmax of the
+    same input equals the window's (exp(-inf) = 0; the kernel never reads those cells), and
+    every element compares with the oracle's tril rows, in blocks of rows."""
+    S, L, lo = 100000, 100000 - 5, -70000
+    dtype = workloads.BF16
+    print(f"band forward S={S} L={L} lo={lo} {DNAME[dtype]}", flush=True)
+    x = workloads.scores_device((1, 1, S, S), dtype, 1.0, 3301)
+    cols = torch.arange(S, device="cuda")
+    for r0 in range(0, S, 4096):
+        r1 = min(S, r0 + 4096)
+        rows = torch.arange(r0, r1, device="cuda")[:, None]
+        x[0, 0, r0:r1].masked_fill_(cols[None, :] < rows + lo, float("-inf"))
+    sl = lens_dev([L])
+    y = g.forward_band(x, sl, lo, 0, 0.125)
+    torch.cuda.synchronize()
+    worst = check_rows_against_oracle(x, y, np.asarray([L], np.int32), 0.125, dtype)
+    print(f"S={S} window {-lo + 1}: every element checked, worst error {worst:.3g}", flush=True)
+    del x, y
+    torch.cuda.empty_cache()
