@@ -47,9 +47,15 @@ struct AttnArgs {
 
 constexpr int kAttnRows = 128;  // query rows per workgroup (4 wavefronts x 32)
 // The accumulators stay scaled to a row's reference max m until a block's max exceeds m by
-// more than this (log2 domain): probabilities then stay below 2^8, and the rescale runs only
+// more than this (log2 domain) on a block that takes the exact path: the rescale then runs only
 // on the few blocks that raise some row's max that far.
 constexpr float kAttnSlack = 8.0f;
+// Blocks after a group's first skip the max: their probabilities, formed against the current
+// reference, are kept when each lane's sum of them is at most this, so every probability is
+// at most 2^15, inside binary16's range (65504). Larger sums take the exact path. After an
+// exact block the reference trails the max by at most kAttnSlack, so a lane's 32 probabilities
+// sum to at most 2^13 and rising maxima keep the fast path for several blocks.
+constexpr float kAttnSumMax = 32768.0f;
 // keys per block: 64 for head size 64, 32 for 128 (keeps two workgroups' registers per SIMD)
 template <int D> constexpr int kAttnKeys = D <= 64 ? 64 : 32;
 
@@ -258,44 +264,62 @@ __global__ __launch_bounds__(256 * SPLIT) __attribute__((amdgpu_waves_per_eu(D <
                     s[st][e] = 32 * st + 8 * (e / 4) + (e & 3) <= lim ? s[st][e] : -INFINITY;
             }
         }
-        // this lane's half of the row: max over its 8 keys per 32-key tile
-        float mh = -INFINITY;
-#pragma unroll
-        for (int st = 0; st < NS; ++st) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) mh = fmaxf(mh, s[st][e]);
-        }
-        // Reference max in the log2 domain. It moves to the running max m' = max over kept
-        // keys of s * k2 only when some row of the wavefront gains more than kAttnSlack
-        // (a wave-uniform branch); the sums are then rescaled by 2^(m - m'). Softmax does
-        // not depend on the reference, so this changes rounding only; every probability
-        // stays below 2^kAttnSlack. A row's max exceeds the bound exactly when one of its two
-        // halves does (m_run is the same on both lanes of a row, and k2 >= 0), so the
-        // wave-wide test runs on the halves and the exchange with lane l ^ 32 that gives
-        // the row max happens only inside the branch.
-        const float mkh = mh == -INFINITY ? -INFINITY : mh * k2;
-        if (__builtin_amdgcn_ballot_w64(mkh > m_run + kAttnSlack) != 0) {
-            const float mb = fmaxf(mh, swap_halves(mh));
-            const float mk = mb == -INFINITY ? -INFINITY : mb * k2;
-            const float m_new = fmaxf(m_run, mk);
-            const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            l_part *= alpha;
-#pragma unroll
-            for (int t = 0; t < NT; ++t) acc[t] *= alpha;
-        }
-        const float m_use = m_run == -INFINITY ? 0.0f : m_run;
-        // probabilities, rounded to the element type for the second product
+        // Probabilities p = 2^(s*k2 - m) against the row's reference m (log2 domain), rounded
+        // to the element type for the second product. Softmax does not depend on the
+        // reference, so it changes rounding only.
         vec8 p[2 * NS];
         float ps = 0.0f;
+        auto probs = [&]() {
+            const float m_use = m_run == -INFINITY ? 0.0f : m_run;
+            ps = 0.0f;
 #pragma unroll
-        for (int st = 0; st < NS; ++st) {
+            for (int st = 0; st < NS; ++st) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][e], k2, -m_use));
-                ps += pe;
-                p[2 * st + e / 8][e % 8] = (elem_t)pe;
+                for (int e = 0; e < 16; ++e) {
+                    const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][e], k2, -m_use));
+                    ps += pe;
+                    p[2 * st + e / 8][e % 8] = (elem_t)pe;
+                }
             }
+        };
+        // Fast path, every block after the group's first: no max. The probabilities are
+        // formed against the current reference and kept when every lane's sum, which bounds
+        // its probabilities, is at most kAttnSumMax (a NaN or infinite sum fails the test).
+        // Otherwise, and on the group's first block, where the rows have no reference yet,
+        // the exact path: the block's max moves the reference when some row gains more than
+        // kAttnSlack, and the probabilities are formed again.
+        bool exact = kb == k_begin;
+        if (!exact) {
+            probs();
+            exact = __builtin_amdgcn_ballot_w64(!(ps <= kAttnSumMax)) != 0;
+        }
+        if (exact) {
+            // this lane's half of the row: max over its 8 keys per 32-key tile
+            float mh = -INFINITY;
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) mh = fmaxf(mh, s[st][e]);
+            }
+            // The reference moves to the running max m' = max over kept keys of s * k2 only
+            // when some row of the wavefront gains more than kAttnSlack (a wave-uniform
+            // branch); the sums are then rescaled by 2^(m - m'), and every probability stays
+            // below 2^kAttnSlack. A row's max exceeds the bound exactly when one of its two
+            // halves does (m_run is the same on both lanes of a row, and k2 >= 0), so the
+            // wave-wide test runs on the halves and the exchange with lane l ^ 32 that gives
+            // the row max happens only inside the branch.
+            const float mkh = mh == -INFINITY ? -INFINITY : mh * k2;
+            if (__builtin_amdgcn_ballot_w64(mkh > m_run + kAttnSlack) != 0) {
+                const float mb = fmaxf(mh, swap_halves(mh));
+                const float mk = mb == -INFINITY ? -INFINITY : mb * k2;
+                const float m_new = fmaxf(m_run, mk);
+                const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+                m_run = m_new;
+                l_part *= alpha;
+#pragma unroll
+                for (int t = 0; t < NT; ++t) acc[t] *= alpha;
+            }
+            probs();
         }
         l_part += ps;
         // O^T[d][row] += V^T[d][keys] P^T[keys][row]; vector 2*st + h covers the lane's keys
