@@ -282,7 +282,8 @@ def test_backward_full_long_bf16_2x1x100000():
 
 def test_backward_stash_rows():
     """Rows past 8 vectors per lane that the LDS stash takes: binary32 rows of 40000 (10000
-    vectors, 8192 of them in registers), and a bfloat16 causal window of 70001 columns on rows
+    vectors, 8192 of them in registers), binary16 rows of 70000 (8750 vectors plus up to 6 of
+    line slack), and a bfloat16 causal window of 70001 columns on rows
     of 100000, whose rows hold only their interval (up to 8766 vectors). y is uniform in
     [0, 2/n) over the kept set (n its width) and zero elsewhere, dy normal. With y zero
     outside the window, D and every kept dx of the window equal those of the grouped tril
@@ -290,6 +291,7 @@ def test_backward_stash_rows():
     masked elements must also be +0 bit for bit. Paired rows and dx written over dy give the
     same bits."""
     cases = ((workloads.F32, 40000, 40000 - 3, None, 0.7),
+             (workloads.F16, 70000, 70000 - 9, None, 0.45),
              (workloads.BF16, 100000, 100000 - 5, -70000, 0.3))
     for dtype, S, L, lo, scale in cases:
         print(f"backward stash rows S={S} dtype={DNAME[dtype]} L={L} lo={lo}", flush=True)

@@ -181,12 +181,14 @@ def test_long_rows_every_path():
 
 def test_very_long_rows_every_element():
     """Rows at the block path's widest layout, where each lane keeps sixteen raw 16-byte
-    vectors (bfloat16 100000 through the automatic choice, 12.2 vectors per lane with the
-    last one partly used; binary32 65536 forced, exactly sixteen), beyond it (binary32 70000,
-    the stream path) and at the automatic eight vectors per lane (binary16 40000): every
-    element against the oracle, in blocks of 1024 rows through its row entry point."""
+    vectors (bfloat16 100000 and binary16 90000 through the automatic choice, 12.2 and 11
+    vectors per lane with the last one partly used; binary32 65536 forced, exactly sixteen),
+    beyond it (binary32 70000, the stream path) and at the automatic eight vectors per lane
+    (binary16 40000): every element against the oracle, in blocks of 1024 rows through its
+    row entry point."""
     for dtype, S, path in ((workloads.F32, 70000, "stream"), (workloads.F32, 65536, "block"),
-                           (workloads.BF16, 100000, "auto"), (workloads.F16, 40000, "auto")):
+                           (workloads.BF16, 100000, "auto"), (workloads.F16, 90000, "auto"),
+                           (workloads.F16, 40000, "auto")):
         lens = [S - 17]
         print(f"very long rows S={S} dtype={DNAME[dtype]} path={path}", flush=True)
         x = workloads.scores_device((1, 1, S, S), dtype, 1.0, seed=7000 + S)
