@@ -417,17 +417,22 @@ def test_side_stream_and_graph_replay():
 def test_full_long_bf16_2x1x100000():
     """Rows of 100000 bfloat16 elements (the block path at sixteen raw vectors per lane) at the
     benchmark's size, lengths 100000 and 70000: every element against the oracle, in blocks of
-    1024 rows through the oracle's row entry point."""
+    1024 rows through the oracle's row entry point; the band [-S, 0] (the same kept set, row-
+    relative slots) gives the same bits."""
     name = "long_bf16_2x1x100000"
     w = workloads.WORKLOADS[name]
     lens = workloads.seq_lens(w)
     print(f"full workload {name} lens={list(lens)}", flush=True)
     x = workloads.scores_device(w.shape, w.dtype, w.sigma, w.x_seed)
-    y = g.forward(x, torch.as_tensor(lens).cuda(), w.scale)
+    sl = torch.as_tensor(lens).cuda()
+    y = g.forward(x, sl, w.scale)
     torch.cuda.synchronize()
     worst = check_rows_against_oracle(x, y, lens, w.scale, w.dtype)
     print(f"{name}: every element checked, worst error {worst:.3g}", flush=True)
-    del x, y
+    yb = g.forward_band(x, sl, -w.S, 0, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(yb.view(torch.int16), y.view(torch.int16)), "band [-S, 0] changed bits"
+    del x, y, yb
     torch.cuda.empty_cache()
 
 
