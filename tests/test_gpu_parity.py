@@ -414,6 +414,47 @@ def test_side_stream_and_graph_replay():
         torch.cuda.synchronize()
 
 
+def test_graph_replay_variants_and_attention():
+    """A captured HIP graph of the band and explicit-mask forwards, the band backward and the
+    fused attention (whole tiles and the key split) replays to the eager calls' bits, three
+    times, with eager work and synchronisations between the replays."""
+    S, lens = 300, [300, 123, 0]
+    x = workloads.scores_cpu((3, 2, S, S), workloads.BF16, 1.0, 91).cuda()
+    dy = workloads.scores_cpu((3, 2, S, S), workloads.BF16, 1.0, 92).cuda()
+    sl = torch.as_tensor(np.asarray(lens, np.int32)).cuda()
+    mask = torch.ones(S, S, dtype=torch.uint8, device="cuda").tril_(5)[None, None]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(93)
+    Sa = 2048  # long enough for the key split
+    q, k, v = (torch.randn((2, 2, Sa, 64), generator=gen, device="cuda").to(torch.bfloat16)
+               for _ in range(3))
+    sla = torch.as_tensor(np.asarray([Sa, 1500], np.int32)).cuda()
+
+    def run(outs):
+        g.forward_band(x, sl, -40, 0, 0.5, out=outs[0])
+        g.forward_masked(x, mask, sl, 0.5, out=outs[1])
+        g.backward_band(outs[0], dy, sl, -40, 0, 0.5, out=outs[2])
+        g.attention(q, k, v, sla, 0.125, out=outs[3], split="off")
+        g.attention(q, k, v, sla, 0.125, out=outs[4], split="on")
+
+    ref = [torch.empty_like(x) for _ in range(3)] + [torch.empty_like(q) for _ in range(2)]
+    run(ref)
+    torch.cuda.synchronize()
+    outs = [torch.empty_like(t) for t in ref]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(outs)
+    for i in range(3):
+        for t in outs:
+            t.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for j, (a, b) in enumerate(zip(outs, ref)):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"replay {i} output {j}"
+        g.forward_band(x, sl, -7, 3, 0.25)  # eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_full_long_bf16_2x1x100000():
     """Rows of 100000 bfloat16 elements (the block path at sixteen raw vectors per lane) at the
     benchmark's size, lengths 100000 and 70000: every element against the oracle, in blocks of

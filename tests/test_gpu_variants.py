@@ -321,6 +321,44 @@ def test_variants_block_rows_every_element():
         torch.cuda.empty_cache()
 
 
+def test_shared_mask_long_rows_every_element():
+    """A [1, 1, S, S] mask shared by 2 x 2 planes on binary16 rows of 33000 (66000 bytes: the
+    rows are long enough for the unit order that takes blocks of 64 rows plane after plane,
+    and 33000 = 515 * 64 + 40 leaves a shorter last block). The mask is the lower triangle
+    of ones, which with the valid lengths keeps exactly the grouped tril set, so every
+    element compares with the oracle's tril row entry points, forward and backward. The same
+    mask materialised per plane (non-zero strides, so the plane-major order) gives the same
+    bits."""
+    dtype, S, B, M = workloads.F16, 33000, 2, 2
+    lens = np.asarray([S - 17, S - 3001], np.int32)
+    sl = lens_dev(lens)
+    print(f"shared mask long rows S={S} B={B} M={M} lens={list(lens)}", flush=True)
+    tril = torch.ones((S, S), dtype=torch.uint8, device="cuda").tril_()[None, None]
+    x = workloads.scores_device((B, M, S, S), dtype, 1.0, S + 5)
+    y = g.forward_masked(x, tril, sl, 0.5)
+    torch.cuda.synchronize()
+    worst = check_rows_against_oracle(x, y, lens, 0.5, dtype)
+    print(f"shared mask forward: every element checked, worst error {worst:.3g}", flush=True)
+    per_plane = tril.expand(B, M, S, S).contiguous()
+    y2 = g.forward_masked(x, per_plane, sl, 0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), \
+        "shared and per-plane masks differ (forward)"
+    del x, y2
+    torch.cuda.empty_cache()
+    dy = workloads.scores_device((B, M, S, S), dtype, 1.0, S + 6)
+    dx = g.backward_masked(y, dy, tril, sl, 0.5)
+    torch.cuda.synchronize()
+    worst = check_rows_backward_against_oracle(y, dy, dx, lens, 0.5, dtype, U[dtype], TINY[dtype])
+    print(f"shared mask backward: every element checked, worst error {worst:.3g}", flush=True)
+    dx2 = g.backward_masked(y, dy, per_plane, sl, 0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(dx.view(torch.int16), dx2.view(torch.int16)), \
+        "shared and per-plane masks differ (backward)"
+    del y, dy, dx, dx2, per_plane, tril
+    torch.cuda.empty_cache()
+
+
 def test_full_size_window_and_key_masks():
     """Full workload shapes, every element of every plane against the oracle: a causal window
     of 512 columns on binary16 32 x 1 x 4096, and per-sample key masks [B, 1, 1, S] (the

@@ -152,7 +152,7 @@ __global__ __launch_bounds__(WPB * kWave) void bwd_wave(FwdArgs a) {
     const uint32_t blk = (a.flags & F_XCD) ? xcd_chunked(blockIdx.x, nblk, a.xcd_shift) : blockIdx.x;
     for (uint64_t unit = (uint64_t)blk * WPB + wave; unit < a.n_units;
          unit += (uint64_t)nblk * WPB) {
-        const Unit u = decode_unit((uint32_t)unit, a);
+        const Unit u = decode_unit<MK, false>((uint32_t)unit, a);
         const int L = valid_len<MK>(a, u.plane);
         bwd_wave_row<DT, WIDE, NV, SP, MK>(a, u.plane, u.r0, L, lane);
         if (u.r1 >= 0) bwd_wave_row<DT, WIDE, NV, SP, MK>(a, u.plane, u.r1, L, lane);
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(W * kWave) void bwd_block(FwdArgs a) {
     const uint32_t nblk = gridDim.x;
     const uint32_t blk = (a.flags & F_XCD) ? xcd_chunked(blockIdx.x, nblk, a.xcd_shift) : blockIdx.x;
     for (uint64_t unit = blk; unit < a.n_units; unit += nblk) {
-        const Unit u = decode_unit((uint32_t)unit, a);
+        const Unit u = decode_unit<MK, (W >= 8)>((uint32_t)unit, a);
         const int L = valid_len<MK>(a, u.plane);
         bwd_block_row<DT, WIDE, NV, W, SP, MK>(a, u.plane, u.r0, L, part[0]);
         if (u.r1 >= 0) bwd_block_row<DT, WIDE, NV, W, SP, MK>(a, u.plane, u.r1, L, part[1]);
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(W * kWave) void bwd_stash(FwdArgs a) {
     const uint32_t nblk = gridDim.x;
     const uint32_t blk = (a.flags & F_XCD) ? xcd_chunked(blockIdx.x, nblk, a.xcd_shift) : blockIdx.x;
     for (uint64_t unit = blk; unit < a.n_units; unit += nblk) {
-        const Unit u = decode_unit((uint32_t)unit, a);
+        const Unit u = decode_unit<MK, false>((uint32_t)unit, a);
         const int L = valid_len<MK>(a, u.plane);
         bwd_stash_row<DT, NV, W, SP, MK>(a, u.plane, u.r0, L, part[0], ys, gs);
         if (u.r1 >= 0) bwd_stash_row<DT, NV, W, SP, MK>(a, u.plane, u.r1, L, part[1], ys, gs);
@@ -413,7 +413,7 @@ __global__ __launch_bounds__(W * kWave) void bwd_stream(FwdArgs a) {
     const uint32_t nblk = gridDim.x;
     const uint32_t blk = (a.flags & F_XCD) ? xcd_chunked(blockIdx.x, nblk, a.xcd_shift) : blockIdx.x;
     for (uint64_t unit = blk; unit < a.n_units; unit += nblk) {
-        const Unit u = decode_unit((uint32_t)unit, a);
+        const Unit u = decode_unit<MK, true>((uint32_t)unit, a);
         const int L = valid_len<MK>(a, u.plane);
         bwd_stream_row<DT, WIDE, W, SP, MK>(a, u.plane, u.r0, L, part[0]);
         if (u.r1 >= 0) bwd_stream_row<DT, WIDE, W, SP, MK>(a, u.plane, u.r1, L, part[1]);

@@ -33,6 +33,9 @@
 // S+1 columns whatever r is. Units are taken in row order, each XCD working through chunks
 // of consecutive workgroups (xcd_chunked): the rows written at any moment then sit close
 // together in memory, which HBM rewards (measured on MI355X: pairing rows cost 5-10%).
+// With an explicit mask whose rows several planes share (F_ACROSS), units run in blocks of
+// rows taken plane after plane, so that the planes' uses of one mask row fall together in
+// time while the rows written still form runs of whole blocks.
 //
 // Mask variants (page "优化ScaledMaskSoftmax算子", the ScaledMaskSoftmax article): masked
 // scores count as minus infinity (section 2.1), a row with no kept element is zeros
@@ -51,7 +54,7 @@
 
 namespace gtms {
 
-enum : unsigned { F_PAIR = 1u, F_XCD = 2u, F_LINES = 4u, F_IVREL = 8u };
+enum : unsigned { F_PAIR = 1u, F_XCD = 2u, F_LINES = 4u, F_IVREL = 8u, F_ACROSS = 16u };
 enum : int { MK_TRIL = 0, MK_BAND = 1, MK_MASK = 2 };
 
 
@@ -71,6 +74,7 @@ struct FwdArgs {
     float k;                   // forward: scale * log2(e); backward: scale
     unsigned flags;
     uint32_t xcd_shift;        // F_XCD: log2 of the blocks in one XCD chunk
+    uint32_t across_shift;     // F_ACROSS: log2 of the rows per block of the unit order
     int lo, hi;                // MK_BAND: kept when lo <= c - r <= hi (clamped to [-S, S])
     const uint8_t* mask;       // MK_MASK: element (b, m, r, c) at mask[b*sb + m*sm + r*sr + c]
     int64_t mask_sb, mask_sm, mask_sr;
@@ -81,10 +85,33 @@ struct Unit {
     int r0, r1;  // rows of the unit; r1 < 0 when the unit is one row
 };
 
+// ACROSS: the kernel honours F_ACROSS (compiled into the kernels of long rows only: the block
+// path at 8 or more wavefronts per row and the stream path); the others ignore the flag,
+// which changes the order of the units and nothing else.
+template <int MK, bool ACROSS>
 __device__ __forceinline__ Unit decode_unit(uint32_t unit, const FwdArgs& a) {
     Unit u;
-    u.plane = unit / a.units_per_plane;
-    u.r0 = (int)(unit - u.plane * a.units_per_plane);
+    if (MK == MK_MASK && ACROSS && (a.flags & F_ACROSS)) {
+        // blocks of R = 2^across_shift rows, each taken plane after plane:
+        // unit = (rb * n_planes + plane) * R + (r0 - rb * R); the last, shorter block of
+        // T < R rows follows as unit = full_units + plane * T + (r0 - full * R)
+        const uint32_t sh = a.across_shift;
+        const uint32_t full = a.units_per_plane >> sh;  // whole blocks per plane
+        const uint32_t full_units = (full * a.n_planes) << sh;
+        if (unit < full_units) {
+            const uint32_t per = a.n_planes << sh;  // at most n_units, as full >= 1
+            const uint32_t rb = unit / per, rem = unit - rb * per;
+            u.plane = rem >> sh;
+            u.r0 = (int)((rb << sh) + (rem & ((1u << sh) - 1)));
+        } else {
+            const uint32_t t = unit - full_units, T = a.units_per_plane - (full << sh);
+            u.plane = t / T;
+            u.r0 = (int)((full << sh) + (t - u.plane * T));
+        }
+    } else {  // unit = plane * units_per_plane + r0
+        u.plane = unit / a.units_per_plane;
+        u.r0 = (int)(unit - u.plane * a.units_per_plane);
+    }
     const int partner = a.S - 1 - u.r0;
     u.r1 = !(a.flags & F_PAIR) || partner == u.r0 ? -1 : partner;
     return u;
@@ -564,7 +591,7 @@ __global__ __launch_bounds__(WPB * kWave) void fwd_wave(FwdArgs a) {
     const uint32_t blk = (a.flags & F_XCD) ? xcd_chunked(blockIdx.x, nblk, a.xcd_shift) : blockIdx.x;
     for (uint64_t unit = (uint64_t)blk * WPB + wave; unit < a.n_units;
          unit += (uint64_t)nblk * WPB) {
-        const Unit u = decode_unit((uint32_t)unit, a);
+        const Unit u = decode_unit<MK, false>((uint32_t)unit, a);
         const int L = valid_len<MK>(a, u.plane);
         wave_row<DT, WIDE, NV, SP, MK>(a, u.plane, u.r0, L, lane);
         if (u.r1 >= 0) wave_row<DT, WIDE, NV, SP, MK>(a, u.plane, u.r1, L, lane);
@@ -644,7 +671,7 @@ __global__ __launch_bounds__(W * kWave) void fwd_block(FwdArgs a) {
     const uint32_t nblk = gridDim.x;
     const uint32_t blk = (a.flags & F_XCD) ? xcd_chunked(blockIdx.x, nblk, a.xcd_shift) : blockIdx.x;
     for (uint64_t unit = blk; unit < a.n_units; unit += nblk) {
-        const Unit u = decode_unit((uint32_t)unit, a);
+        const Unit u = decode_unit<MK, (W >= 8)>((uint32_t)unit, a);
         const int L = valid_len<MK>(a, u.plane);
         block_row<DT, WIDE, NV, W, SP, MK>(a, u.plane, u.r0, L, part[0][0], part[0][1]);
         if (u.r1 >= 0)
@@ -735,7 +762,7 @@ __global__ __launch_bounds__(W * kWave) void fwd_stream(FwdArgs a) {
     const uint32_t nblk = gridDim.x;
     const uint32_t blk = (a.flags & F_XCD) ? xcd_chunked(blockIdx.x, nblk, a.xcd_shift) : blockIdx.x;
     for (uint64_t unit = blk; unit < a.n_units; unit += nblk) {
-        const Unit u = decode_unit((uint32_t)unit, a);
+        const Unit u = decode_unit<MK, true>((uint32_t)unit, a);
         const int L = valid_len<MK>(a, u.plane);
         stream_row<DT, WIDE, W, SP, MK>(a, u.plane, u.r0, L, part[0][0], part[0][1]);
         if (u.r1 >= 0) stream_row<DT, WIDE, W, SP, MK>(a, u.plane, u.r1, L, part[1][0], part[1][1]);
