@@ -355,7 +355,28 @@ def test_shared_mask_long_rows_every_element():
     torch.cuda.synchronize()
     assert torch.equal(dx.view(torch.int16), dx2.view(torch.int16)), \
         "shared and per-plane masks differ (backward)"
-    del y, dy, dx, dx2, per_plane, tril
+    del dx, dx2
+    torch.cuda.empty_cache()
+    # The stream path (forced) takes the same order with the shared mask: into outputs
+    # filled with NaN, both orders must write the same bits everywhere (a unit skipped or
+    # visited twice would leave NaN behind). Its arithmetic is checked against the oracle
+    # in the path sweeps.
+    x = workloads.scores_device((B, M, S, S), dtype, 1.0, S + 5)
+    for tag, run in (
+            ("forward", lambda m, o: g.forward_masked(x, m, sl, 0.5, out=o, path="stream")),
+            ("backward", lambda m, o: g.backward_masked(y, dy, m, sl, 0.5, out=o, path="stream"))):
+        a = torch.full_like(x, float("nan"))
+        b = torch.full_like(x, float("nan"))
+        run(tril, a)
+        run(per_plane, b)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), \
+            f"stream path: shared and per-plane masks differ ({tag})"
+        assert not torch.isnan(a).any(), f"stream path: unwritten elements ({tag})"
+        print(f"shared mask stream {tag}: same bits as the per-plane mask", flush=True)
+        del a, b
+        torch.cuda.empty_cache()
+    del x, y, dy, per_plane, tril
     torch.cuda.empty_cache()
 
 
