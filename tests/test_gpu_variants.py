@@ -328,7 +328,8 @@ def test_shared_mask_long_rows_every_element():
     of ones, which with the valid lengths keeps exactly the grouped tril set, so every
     element compares with the oracle's tril row entry points, forward and backward. The same
     mask materialised per plane (non-zero strides, so the plane-major order) gives the same
-    bits."""
+    bits, and so do paired rows (the order's blocks then run over pair indices) and the
+    stream path with either mask."""
     dtype, S, B, M = workloads.F16, 33000, 2, 2
     lens = np.asarray([S - 17, S - 3001], np.int32)
     sl = lens_dev(lens)
@@ -344,6 +345,11 @@ def test_shared_mask_long_rows_every_element():
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), \
         "shared and per-plane masks differ (forward)"
+    # rows paired (r, S-1-r): the blocks of the order then run over pair indices
+    y2 = g.forward_masked(x, tril, sl, 0.5, flags=g.FLAG_PAIR_ROWS)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), \
+        "paired rows differ (forward)"
     del x, y2
     torch.cuda.empty_cache()
     dy = workloads.scores_device((B, M, S, S), dtype, 1.0, S + 6)
@@ -355,6 +361,10 @@ def test_shared_mask_long_rows_every_element():
     torch.cuda.synchronize()
     assert torch.equal(dx.view(torch.int16), dx2.view(torch.int16)), \
         "shared and per-plane masks differ (backward)"
+    dx2 = g.backward_masked(y, dy, tril, sl, 0.5, flags=g.FLAG_PAIR_ROWS)
+    torch.cuda.synchronize()
+    assert torch.equal(dx.view(torch.int16), dx2.view(torch.int16)), \
+        "paired rows differ (backward)"
     del dx, dx2
     torch.cuda.empty_cache()
     # The stream path (forced) takes the same order with the shared mask: into outputs
