@@ -141,6 +141,37 @@ def test_masked_layouts(dtype):
                             as_bool=(li % 2 == 1))
 
 
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DNAME[d])
+def test_variants_in_place(dtype):
+    """The variants follow gtms_forward's and gtms_backward's in-place rules: the band and the
+    explicit-mask forwards with out = x, and their backwards with dx = dy, give the bits of
+    the calls into separate outputs, on every path the rows fit."""
+    B, M = 2, 2
+    for S, lens in ((300, [300, 123]), (1030, [1030, 517])):
+        sl = lens_dev(lens)
+        rng = np.random.default_rng(S)
+        mask = torch.as_tensor((rng.uniform(size=(1, M, S, S)) < 0.7).astype(np.uint8)).cuda()
+        x = workloads.scores_cpu((B, M, S, S), dtype, 1.0, S + 11).cuda()
+        dy = workloads.scores_cpu((B, M, S, S), dtype, 1.0, S + 12).cuda()
+        ib = torch.int32 if dtype == workloads.F32 else torch.int16
+        for path in [p for p in PATHS if path_ok(p, S, dtype)]:
+            print(f"variants in place S={S} {DNAME[dtype]} path={path}", flush=True)
+            for tag, fwd, bwd in (
+                    ("band", lambda t, o: g.forward_band(t, sl, -40, 3, 0.7, out=o, path=path),
+                     lambda y, d, o: g.backward_band(y, d, sl, -40, 3, 0.7, out=o, path=path)),
+                    ("mask", lambda t, o: g.forward_masked(t, mask, sl, 0.7, out=o, path=path),
+                     lambda y, d, o: g.backward_masked(y, d, mask, sl, 0.7, out=o, path=path))):
+                y = fwd(x, None)
+                xi = x.clone()
+                fwd(xi, xi)
+                dx = bwd(y, dy, None)
+                dyi = dy.clone()
+                bwd(y, dyi, dyi)
+                torch.cuda.synchronize()
+                assert torch.equal(xi.view(ib), y.view(ib)), f"{tag} forward in place, {path}"
+                assert torch.equal(dyi.view(ib), dx.view(ib)), f"{tag} backward in place, {path}"
+
+
 def test_masked_unaligned_mask_rows():
     """Mask rows at odd byte strides (a view into a wider buffer): the element-wise path."""
     for dtype, S in ((workloads.F32, 256), (workloads.BF16, 1000)):
